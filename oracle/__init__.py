@@ -1,0 +1,147 @@
+"""ctypes wrapper of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the benchmark's
+CPU-baseline leg, never by the library package.  It shares nothing with the HIP
+path; inputs come from `workloads`, which holds no arithmetic of the method.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc: -O2, no fast-math, no contraction, OpenMP."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-o", tmp, SRC_PATH, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        i64, sz, p = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+        L.oracle_threads.restype = ctypes.c_int
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.tq2_oracle_dequant.argtypes = [p, sz, i64, i64, p]
+        L.tq2_oracle_gemm.argtypes = [p, sz, i64, i64, p, i64, p, p]
+        L.tq2_oracle_gemm_at.argtypes = [p, sz, i64, i64, p, i64, p, p, i64, p, p]
+        L.tq2_oracle_gemm_f32seq.argtypes = [p, sz, i64, i64, p, i64, p]
+        L.blr_oracle_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p, p]
+        L.blr_oracle_bound_at.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        for f in ("tq2_oracle_dequant", "tq2_oracle_gemm", "tq2_oracle_gemm_at",
+                  "tq2_oracle_gemm_f32seq", "blr_oracle_forward", "blr_oracle_bound_at"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
+
+
+def half_to_double(bits: int) -> float:
+    return float(lib().oracle_half_to_double(bits))
+
+
+def dequant(aos, n: int, k: int) -> np.ndarray:
+    aos = _c(aos, np.uint8)
+    w = np.empty((n, k), dtype=np.float32)
+    _check(lib().tq2_oracle_dequant(_ptr(aos), aos.size, n, k, _ptr(w)))
+    return w
+
+
+def gemm(aos, n: int, k: int, x):
+    """(y64 [M][N] float64, bound [M][N] float64) for y = x @ W^T."""
+    aos = _c(aos, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    m = x.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    b = np.empty((m, n), dtype=np.float64)
+    _check(lib().tq2_oracle_gemm(_ptr(aos), aos.size, n, k, _ptr(x), m, _ptr(y), _ptr(b)))
+    return y, b
+
+
+def gemm_at(aos, n: int, k: int, x, mi, ni):
+    """Selected outputs (mi[s], ni[s]): (y64 [S], bound [S])."""
+    aos = _c(aos, np.uint8)
+    x = _c(x, np.float32)
+    mi = _c(mi, np.int64)
+    ni = _c(ni, np.int64)
+    y = np.empty(mi.size, dtype=np.float64)
+    b = np.empty(mi.size, dtype=np.float64)
+    _check(lib().tq2_oracle_gemm_at(_ptr(aos), aos.size, n, k, _ptr(x), x.shape[0],
+                                    _ptr(mi), _ptr(ni), mi.size, _ptr(y), _ptr(b)))
+    return y, b
+
+
+def gemm_f32seq(aos, n: int, k: int, x) -> np.ndarray:
+    """The correctness test's f32 sequential-accumulation reference."""
+    aos = _c(aos, np.uint8)
+    x = _c(x, np.float32)
+    y = np.empty((x.shape[0], n), dtype=np.float32)
+    _check(lib().tq2_oracle_gemm_f32seq(_ptr(aos), aos.size, n, k, _ptr(x), x.shape[0], _ptr(y)))
+    return y
+
+
+def blr_forward(bits_u, bits_v, h, l, g, x, want_a: bool = False):
+    """(y64 [M][d_out], a64 [M][r] or None)."""
+    bits_u = _c(bits_u, np.uint32)
+    bits_v = _c(bits_v, np.uint32)
+    h, l, g, x = (_c(v, np.float32) for v in (h, l, g, x))
+    m, d_in = x.shape
+    d_out, r = h.size, l.size
+    y = np.empty((m, d_out), dtype=np.float64)
+    a = np.empty((m, r), dtype=np.float64) if want_a else None
+    _check(lib().blr_oracle_forward(_ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l), _ptr(g), _ptr(x),
+                                    m, d_in, d_out, r, _ptr(y), _ptr(a)))
+    return y, a
+
+
+def blr_bound_at(bits_u, bits_v, h, l, g, x, ti, ii) -> np.ndarray:
+    bits_u = _c(bits_u, np.uint32)
+    bits_v = _c(bits_v, np.uint32)
+    h, l, g, x = (_c(v, np.float32) for v in (h, l, g, x))
+    ti = _c(ti, np.int64)
+    ii = _c(ii, np.int64)
+    m, d_in = x.shape
+    b = np.empty(ti.size, dtype=np.float64)
+    _check(lib().blr_oracle_bound_at(_ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l), _ptr(g), _ptr(x),
+                                     m, d_in, h.size, l.size, _ptr(ti), _ptr(ii), ti.size, _ptr(b)))
+    return b
