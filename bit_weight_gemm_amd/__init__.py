@@ -1,0 +1,222 @@
+"""Python binding of libtq2 (ctypes): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libtq2.so; torch only
+supplies device memory (tensors on the current GPU) and the current stream.
+There is no CPU fallback: if the library is missing or fails to load, the calls
+raise.
+
+Names follow the C ABI in include/libtq2.h: tq2_upload, tq2_free, tq2_gemm,
+tq2_gemm_path, tq2_dequant, blr_forward, blr_workspace_size, tq2_select_path,
+tq2_set_m_small, tq2_strerror, tq2_version.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq2.so")
+
+TQ2_OK, TQ2_EINVAL, TQ2_ENOMEM, TQ2_EDEVICE, TQ2_ENODEV = 0, -1, -2, -3, -4
+TQ2_PATH_AUTO, TQ2_PATH_F32, TQ2_PATH_MFMA = 0, 1, 2
+
+_lib = None
+
+
+class Tq2Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {tq2_strerror(status)} ({status})")
+
+
+def _single_hip_runtime():
+    """Fail if two different HIP runtimes are mapped (device pointers would not mix)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise RuntimeError(f"more than one HIP runtime loaded: {sorted(real)}")
+
+
+def lib():
+    """Load libtq2.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- load torch's HIP runtime first
+
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run bit_weight_gemm_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    _single_hip_runtime()
+    i64, sz, p, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "tq2_upload": ([p, sz, i64, i64, p, ctypes.POINTER(p)], i32),
+        "tq2_free": ([p], i32),
+        "tq2_weight_info": ([p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(sz)], i32),
+        "tq2_gemm": ([p, p, p, i64, i64, i64, p], i32),
+        "tq2_gemm_path": ([p, p, p, i64, i64, i64, i32, p], i32),
+        "tq2_select_path": ([i64], i32),
+        "tq2_set_m_small": ([i64], i64),
+        "tq2_dequant": ([p, p, p], i32),
+        "blr_workspace_size": ([i64, i64, i64, i64], sz),
+        "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "tq2_strerror": ([i32], ctypes.c_char_p),
+        "tq2_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != TQ2_OK:
+        raise Tq2Error(status, what)
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, dtype, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def tq2_strerror(status: int) -> str:
+    return lib().tq2_strerror(int(status)).decode()
+
+
+def tq2_version() -> str:
+    return lib().tq2_version().decode()
+
+
+def tq2_select_path(m: int) -> int:
+    return int(lib().tq2_select_path(int(m)))
+
+
+def tq2_set_m_small(v: int) -> int:
+    return int(lib().tq2_set_m_small(int(v)))
+
+
+def blr_workspace_size(m: int, d_in: int, d_out: int, r: int) -> int:
+    return int(lib().blr_workspace_size(int(m), int(d_in), int(d_out), int(r)))
+
+
+class Tq2Weight:
+    """Device handle of an uploaded TQ2_0_g128 weight [N][K]; freed on close()/GC."""
+
+    def __init__(self, handle: ctypes.c_void_p, n: int, k: int):
+        self._h = handle
+        self.N, self.K = n, k
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("weight already freed")
+        return self._h
+
+    def device_bytes(self) -> int:
+        nb = ctypes.c_size_t()
+        _check(lib().tq2_weight_info(self.handle, None, None, ctypes.byref(nb)), "tq2_weight_info")
+        return nb.value
+
+    def close(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(lib().tq2_free(h), "tq2_free")
+
+    def __del__(self):
+        try:
+            if self._h is not None and _lib is not None:
+                _lib.tq2_free(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+
+def tq2_upload(aos, n: int, k: int, stream=None) -> Tq2Weight:
+    """Upload AoS block bytes (numpy uint8 / bytes) for a weight [n][k]."""
+    buf = np.ascontiguousarray(np.frombuffer(aos, np.uint8) if isinstance(aos, (bytes, bytearray)) else aos,
+                               dtype=np.uint8)
+    out = ctypes.c_void_p()
+    _check(lib().tq2_upload(buf.ctypes.data_as(ctypes.c_void_p), buf.size, int(n), int(k), _stream(stream),
+                            ctypes.byref(out)), "tq2_upload")
+    return Tq2Weight(out, int(n), int(k))
+
+
+def tq2_free(w: Tq2Weight):
+    w.close()
+
+
+def tq2_gemm_path(w: Tq2Weight, x, y=None, path: int = TQ2_PATH_AUTO, stream=None):
+    """y[M][N] = x[M][K] @ W^T on the chosen path; returns y (allocated if None)."""
+    import torch
+
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [M, {w.K}]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, w.N), dtype=torch.float32, device=x.device)
+    if y.shape != (m, w.N):
+        raise ValueError(f"y must be [{m}, {w.N}]")
+    _check(lib().tq2_gemm_path(w.handle, _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m, w.N, w.K,
+                               int(path), _stream(stream)), "tq2_gemm")
+    return y
+
+
+def tq2_gemm(w: Tq2Weight, x, y=None, stream=None):
+    return tq2_gemm_path(w, x, y, TQ2_PATH_AUTO, stream)
+
+
+def tq2_dequant(w: Tq2Weight, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=torch.float32, device="cuda")
+    if tuple(out.shape) != (w.N, w.K):
+        raise ValueError(f"out must be [{w.N}, {w.K}]")
+    _check(lib().tq2_dequant(w.handle, _dev(out, torch.float32, "out"), _stream(stream)), "tq2_dequant")
+    return out
+
+
+def blr_forward(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
+    """Binary low-rank layer forward; bits_* are int32 tensors holding the u32 bitmap words."""
+    import torch
+
+    m, d_in = x.shape
+    d_out, r = h.numel(), l.numel()
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
+    need = blr_workspace_size(m, d_in, d_out, r)
+    if need == 0:
+        raise Tq2Error(TQ2_EINVAL, "blr_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().blr_forward(_dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
+                             _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
+                             _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
+                             _dev(y, torch.float32, "y"), m, d_in, d_out, r,
+                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+           "blr_forward")
+    return y

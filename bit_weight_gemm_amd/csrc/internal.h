@@ -1,0 +1,48 @@
+// Internal declarations shared by the HIP kernel files and the C-ABI layer.
+//
+// Device weight layout (built by tq2_upload from the array-of-structs blocks):
+//   codes  : u32 [Npad][K/16]   one word per 16 consecutive elements of a row.
+//            Element e (0..15) of the group sits in bits 2*(e>>1) + 16*(e&1):
+//            even elements fill the low half, odd elements the high half, each
+//            as the 2-bit code of the block format.  A word thus yields element
+//            pairs (2s, 2s+1) as the two halves of one 32-bit register, the
+//            shape both the f32 path (one pair per decode) and the MFMA operand
+//            (consecutive k in the low/high halves) consume.
+//   scales : u16 [Npad][K/128]  f16 bit pattern of each block's d.
+//   Rows n >= N up to Npad (a multiple of kRowPad) hold code 1 and scale 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq2 {
+
+constexpr int kBlock = 128;      // weights per block
+constexpr int kRowPad = 256;     // device rows are padded to a multiple of this
+
+struct DevWeight {
+    int64_t N = 0, K = 0, Npad = 0;
+    uint32_t *codes = nullptr;   // [Npad][K/16]
+    uint16_t *scales = nullptr;  // [Npad][K/128]
+    size_t bytes = 0;
+    bool mfma_ok = true;         // no code-3 weight with |2d| beyond f16
+};
+
+// Each launcher validates nothing (the C-ABI layer has) and returns the HIP status.
+hipError_t launch_dequant(const DevWeight &w, float *out, hipStream_t s);
+hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
+hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
+
+// Binary low-rank forward.  Workspace carve-up is computed by blr_plan.
+struct BlrPlan {
+    int64_t M, d_in, d_out, r;
+    int64_t kpad1, kpad2;        // padded contraction lengths of GEMM1 (d_in) and GEMM2 (r)
+    int64_t npad1, npad2;        // padded output widths of GEMM1 (r) and GEMM2 (d_out)
+    size_t off_codes_v, off_codes_u, off_a, total;
+};
+BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_blr_forward(const BlrPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,
+                              const float *h, const float *l, const float *g, const float *x, float *y,
+                              void *workspace, hipStream_t s);
+
+}  // namespace tq2

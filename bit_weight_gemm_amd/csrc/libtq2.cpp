@@ -1,0 +1,286 @@
+// C ABI of libtq2: argument checks, host repack of the weight blocks, path choice
+// and kernel launch.  Declarations and the contract live in include/libtq2.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/libtq2.h"
+#include "internal.h"
+
+using tq2::DevWeight;
+
+struct tq2_weight {
+    DevWeight dev;
+    int device = -1;
+};
+
+namespace {
+
+constexpr size_t kBlockBytes = 34;
+
+// gfx950 check, cached per device ordinal.
+int check_device(int *dev_out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TQ2_ENODEV;
+    static std::mutex mu;
+    static std::vector<int> state;  // 0 unknown, 1 ok, -1 not gfx950
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)state.size() <= dev) state.resize(dev + 1, 0);
+    if (state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TQ2_ENODEV;
+        state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    }
+    if (state[dev] != 1) return TQ2_ENODEV;
+    if (dev_out) *dev_out = dev;
+    return TQ2_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+int from_hip(hipError_t e) {
+    if (e == hipSuccess) return TQ2_OK;
+    if (e == hipErrorOutOfMemory) return TQ2_ENOMEM;
+    return TQ2_EDEVICE;
+}
+
+std::atomic<int64_t> g_m_small{-1};
+std::atomic<int> g_forced{-1};  // -1 unread, 0 none, 1 f32, 2 mfma
+
+int64_t m_small() {
+    int64_t v = g_m_small.load();
+    if (v >= 0) return v;
+    const char *s = std::getenv("TQ2_M_SMALL");
+    v = (s && *s) ? std::strtoll(s, nullptr, 10) : 4;
+    if (v < 0) v = 0;
+    int64_t expect = -1;
+    g_m_small.compare_exchange_strong(expect, v);
+    return g_m_small.load();
+}
+
+int forced_path() {
+    int v = g_forced.load();
+    if (v >= 0) return v;
+    const char *s = std::getenv("TQ2_PATH");
+    v = 0;
+    if (s && std::strcmp(s, "f32") == 0) v = TQ2_PATH_F32;
+    if (s && std::strcmp(s, "mfma") == 0) v = TQ2_PATH_MFMA;
+    g_forced.store(v);
+    return v;
+}
+
+// Pair-interleaved group word: element e of the 16 at bits 2*(e>>1) + 16*(e&1).
+inline uint32_t group_word(const uint8_t *qs4) {
+    uint32_t out = 0;
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t code = (qs4[e >> 2] >> (2 * (e & 3))) & 3u;
+        out |= code << (2 * (e >> 1) + 16 * (e & 1));
+    }
+    return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq2_strerror(int status) {
+    switch (status) {
+        case TQ2_OK: return "ok";
+        case TQ2_EINVAL: return "invalid argument";
+        case TQ2_ENOMEM: return "out of memory";
+        case TQ2_EDEVICE: return "HIP call or kernel launch failed";
+        case TQ2_ENODEV: return "no gfx950 HIP device current";
+        default: return "unknown status";
+    }
+}
+
+const char *tq2_version(void) { return "libtq2 0.1 (gfx950)"; }
+
+int64_t tq2_set_m_small(int64_t v) {
+    const int64_t old = m_small();
+    g_m_small.store(v < 0 ? 0 : v);
+    return old;
+}
+
+int tq2_select_path(int64_t M) {
+    const int f = forced_path();
+    if (f) return f;
+    return M <= m_small() ? TQ2_PATH_F32 : TQ2_PATH_MFMA;
+}
+
+int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *stream, tq2_weight **out) {
+    if (!aos || !out) return TQ2_EINVAL;
+    if (N < 1 || K < tq2::kBlock || K % tq2::kBlock) return TQ2_EINVAL;
+    const int64_t kb = K / tq2::kBlock;
+    if (N > (int64_t)1 << 31 || K > (int64_t)1 << 30) return TQ2_EINVAL;
+    if (nbytes != (size_t)N * (size_t)kb * kBlockBytes) return TQ2_EINVAL;
+    *out = nullptr;
+    int dev = -1;
+    int st = check_device(&dev);
+    if (st) return st;
+
+    const uint8_t *src = static_cast<const uint8_t *>(aos);
+    const int64_t npad = (N + tq2::kRowPad - 1) / tq2::kRowPad * tq2::kRowPad;
+    const int64_t kw = K / 16;
+    const size_t codes_bytes = (size_t)npad * kw * 4;
+    const size_t scale_bytes = (size_t)npad * kb * 2;
+    const size_t scale_off = (codes_bytes + 255) / 256 * 256;
+    const size_t total = scale_off + (scale_bytes + 255) / 256 * 256;
+
+    bool mfma_ok = true;
+    std::vector<uint8_t> host;
+    try {
+        host.assign(total, 0);
+    } catch (const std::bad_alloc &) {
+        return TQ2_ENOMEM;
+    }
+    uint32_t *hc = reinterpret_cast<uint32_t *>(host.data());
+    uint16_t *hs = reinterpret_cast<uint16_t *>(host.data() + scale_off);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < kb; ++b) {
+            const uint8_t *blk = src + ((size_t)n * kb + b) * kBlockBytes;
+            const uint16_t d = (uint16_t)(blk[32] | (blk[33] << 8));
+            if (((d >> 10) & 31) == 31) return TQ2_EINVAL;  // NaN or infinite scale
+            bool has3 = false;
+            for (int g = 0; g < 8; ++g) {
+                const uint32_t wv = group_word(blk + 4 * g);
+                has3 |= ((wv & (wv >> 1)) & 0x55555555u) != 0;
+                hc[n * kw + b * 8 + g] = wv;
+            }
+            // |2d| must stay within f16 for the MFMA operand (code 3 = +2d).
+            if (has3 && (d & 0x7fff) > 0x77ff) mfma_ok = false;
+            hs[n * kb + b] = d;
+        }
+    }
+    for (int64_t n = N; n < npad; ++n)
+        for (int64_t g = 0; g < kw; ++g) hc[n * kw + g] = 0x55555555u;  // code 1 = weight 0
+
+    tq2_weight *w = new (std::nothrow) tq2_weight;
+    if (!w) return TQ2_ENOMEM;
+    void *dmem = nullptr;
+    hipError_t e = hipMalloc(&dmem, total);
+    if (e != hipSuccess) {
+        delete w;
+        return from_hip(e);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(dmem, host.data(), total, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        (void)hipFree(dmem);
+        delete w;
+        return from_hip(e);
+    }
+    w->device = dev;
+    w->dev.N = N;
+    w->dev.K = K;
+    w->dev.Npad = npad;
+    w->dev.codes = static_cast<uint32_t *>(dmem);
+    w->dev.scales = reinterpret_cast<uint16_t *>(static_cast<char *>(dmem) + scale_off);
+    w->dev.bytes = total;
+    w->dev.mfma_ok = mfma_ok;
+    *out = w;
+    return TQ2_OK;
+}
+
+int tq2_free(tq2_weight *w) {
+    if (!w) return TQ2_OK;
+    hipError_t e = hipSuccess;
+    if (w->dev.codes) e = hipFree(w->dev.codes);
+    delete w;
+    return from_hip(e);
+}
+
+int tq2_weight_info(const tq2_weight *w, int64_t *N, int64_t *K, size_t *device_bytes) {
+    if (!w) return TQ2_EINVAL;
+    if (N) *N = w->dev.N;
+    if (K) *K = w->dev.K;
+    if (device_bytes) *device_bytes = w->dev.bytes;
+    return TQ2_OK;
+}
+
+static int check_weight_call(const tq2_weight *w, int64_t N, int64_t K, int *dev) {
+    if (!w || N != w->dev.N || K != w->dev.K) return TQ2_EINVAL;
+    int st = check_device(dev);
+    if (st) return st;
+    if (*dev != w->device) return TQ2_EINVAL;  // handle lives on another device
+    return TQ2_OK;
+}
+
+int tq2_gemm_path(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K, int path,
+                  void *stream) {
+    if (M < 0 || path < TQ2_PATH_AUTO || path > TQ2_PATH_MFMA) return TQ2_EINVAL;
+    if (M > ((int64_t)1 << 31) - 1) return TQ2_EINVAL;
+    int dev = -1;
+    int st = check_weight_call(w, N, K, &dev);
+    if (st) return st;
+    if (M == 0) return TQ2_OK;
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return TQ2_EINVAL;
+    if (overlap(x, (size_t)M * K * 4, y, (size_t)M * N * 4)) return TQ2_EINVAL;
+    if (path == TQ2_PATH_AUTO) path = tq2_select_path(M);
+    if (path == TQ2_PATH_MFMA && !w->dev.mfma_ok) path = TQ2_PATH_F32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = (path == TQ2_PATH_F32) ? tq2::launch_gemv_f32(w->dev, x, y, M, s)
+                                          : tq2::launch_gemm_mfma(w->dev, x, y, M, s);
+    return from_hip(e);
+}
+
+int tq2_gemm(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    return tq2_gemm_path(w, x, y, M, N, K, TQ2_PATH_AUTO, stream);
+}
+
+int tq2_dequant(const tq2_weight *w, float *w_out, void *stream) {
+    int dev = -1;
+    if (!w) return TQ2_EINVAL;
+    int st = check_weight_call(w, w->dev.N, w->dev.K, &dev);
+    if (st) return st;
+    if (!w_out || !aligned16(w_out)) return TQ2_EINVAL;
+    return from_hip(tq2::launch_dequant(w->dev, w_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    if (M < 0 || d_in < 1 || d_out < 1 || r < 32 || r % 32) return 0;
+    if (M > ((int64_t)1 << 31) - 1 || d_in > ((int64_t)1 << 30) || d_out > ((int64_t)1 << 30) ||
+        r > ((int64_t)1 << 30))
+        return 0;
+    return tq2::blr_plan(M, d_in, d_out, r).total;
+}
+
+int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    const size_t need = blr_workspace_size(M, d_in, d_out, r);
+    if (need == 0) return TQ2_EINVAL;
+    int dev = -1;
+    int st = check_device(&dev);
+    if (st) return st;
+    if (M == 0) return TQ2_OK;
+    if (!bits_u || !bits_v || !h || !l || !g || !x || !y || !workspace) return TQ2_EINVAL;
+    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TQ2_EINVAL;
+    if (!aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(bits_u) & 3u) ||
+        (reinterpret_cast<uintptr_t>(bits_v) & 3u) || (reinterpret_cast<uintptr_t>(h) & 3u) ||
+        (reinterpret_cast<uintptr_t>(l) & 3u) || (reinterpret_cast<uintptr_t>(g) & 3u))
+        return TQ2_EINVAL;
+    const size_t ybytes = (size_t)M * d_out * 4;
+    if (overlap(y, ybytes, x, (size_t)M * d_in * 4) || overlap(y, ybytes, workspace, need) ||
+        overlap(y, ybytes, bits_u, (size_t)d_out * (r / 32) * 4) ||
+        overlap(y, ybytes, bits_v, (size_t)d_in * (r / 32) * 4) || overlap(y, ybytes, h, (size_t)d_out * 4) ||
+        overlap(y, ybytes, l, (size_t)r * 4) || overlap(y, ybytes, g, (size_t)d_in * 4))
+        return TQ2_EINVAL;
+    const tq2::BlrPlan plan = tq2::blr_plan(M, d_in, d_out, r);
+    return from_hip(tq2::launch_blr_forward(plan, bits_u, bits_v, h, l, g, x, y, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

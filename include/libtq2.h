@@ -1,0 +1,126 @@
+/*
+ * libtq2 -- ternary (TQ2_0_g128) weight GEMM and binary low-rank layer forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI: host or device pointers and sizes only.  Every device pointer
+ * named below is a HIP device allocation owned by the caller (for example the
+ * storage of a torch tensor on the same GPU); it must stay alive until the work
+ * queued on `stream` has finished.  `stream` is a hipStream_t passed as void*;
+ * NULL means the legacy default stream of the current device.  All calls act on
+ * the current HIP device.
+ *
+ * Status codes: every entry point returns TQ2_OK (0) or a negative TQ2_E* code.
+ * Argument errors are detected on the host before anything is queued and leave
+ * the outputs untouched.  Launch failures return TQ2_EDEVICE.  Faults inside a
+ * kernel surface, as usual for HIP, at the caller's next synchronisation.
+ *
+ * Sources, by page title and section:
+ *  [TQ2]  "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs": the correctness test
+ *         defines the block format (128 weights per block: 32 bytes of 2-bit codes,
+ *         four per byte with the first element in the low bits, then an f16
+ *         scale d; codes 0,1,2 = -1,0,+1, w = (code-1)*d), the weight upload
+ *         (get_or_upload_tq2_weight_soa: AoS bytes in, device handle out, free to
+ *         repack) and the product encode_gemm_tq2 (out[m][n] = sum_k x[m][k]*W[n][k],
+ *         row-major [M][N], overwritten).
+ *  [BLR]  "cortiq-engine 0.8.43 -- train_mm.rs": the module header defines the
+ *         binary low-rank layer W^ = diag(h) S_U diag(l) S_V^T diag(g) and its
+ *         forward a = (x.g) S_V, c = (a.l) S_U^T, y = h.c; `expand` fixes the sign
+ *         bitmap (bit j of word w is rank index 32w+j, set = +1, clear = -1);
+ *         `blr_forward` overwrites y and stages x.g and a.l in f16.
+ */
+#ifndef LIBTQ2_H
+#define LIBTQ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TQ2_OK = 0,
+    TQ2_EINVAL = -1,      /* bad argument: shape, size, pointer, alignment, non-finite scale */
+    TQ2_ENOMEM = -2,      /* device or host allocation failed */
+    TQ2_EDEVICE = -3,     /* a HIP call or kernel launch failed */
+    TQ2_ENODEV = -4,      /* no HIP device, or the current device is not gfx950 */
+};
+
+enum {
+    TQ2_PATH_AUTO = 0,    /* choose by M (see tq2_select_path) */
+    TQ2_PATH_F32 = 1,     /* f32 FMA path: |err| <= 1e-5 * sum_k |x*w| per output */
+    TQ2_PATH_MFMA = 2,    /* f16 MFMA path: x rounded to f16, |err| <= 4e-3 * sum_k |x*w| */
+};
+
+/* Opaque device-resident weight.  Owns its device memory until tq2_free. */
+typedef struct tq2_weight tq2_weight;
+
+/* [TQ2] weight upload.  `aos` is host memory holding N*(K/128) blocks of 34 bytes,
+ * row-major over (row, block): 32 code bytes then the f16 scale, little-endian.
+ * Requires N >= 1, K >= 128, K % 128 == 0, nbytes == N*(K/128)*34 and every scale
+ * finite (a NaN or infinite scale is TQ2_EINVAL).  The bytes are repacked on the
+ * host into the device layout and copied on `stream`; the call returns after the
+ * copy has completed, so `aos` may be freed at once.  *out receives the handle. */
+int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *stream, tq2_weight **out);
+
+/* Releases the handle and its device memory (synchronises the device first).
+ * NULL is accepted and ignored. */
+int tq2_free(tq2_weight *w);
+
+/* Shape and device footprint of a handle (any output pointer may be NULL). */
+int tq2_weight_info(const tq2_weight *w, int64_t *N, int64_t *K, size_t *device_bytes);
+
+/* [TQ2] y[m][n] = sum_k x[m][k] * W[n][k] for m < M, n < N.
+ * x: device f32 [M][K] row-major, 16-byte aligned; y: device f32 [M][N] row-major,
+ * 16-byte aligned, overwritten, must not overlap x.  N and K must equal the
+ * handle's.  M == 0 is a successful no-op.  Asynchronous on `stream`.
+ * The path follows tq2_select_path(M); both paths are deterministic (no atomics). */
+int tq2_gemm(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* tq2_gemm on an explicitly chosen path (TQ2_PATH_AUTO, _F32 or _MFMA).
+ * The MFMA path needs |x| <= 65504 (f16 range; not checked).  A weight holding a
+ * code-3 weight whose scale has |d| > 32752 (2d beyond f16) runs on the f32 path. */
+int tq2_gemm_path(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K,
+                  int path, void *stream);
+
+/* Path that TQ2_PATH_AUTO picks for a product with M rows.  The threshold is the
+ * process default (tq2_set_m_small, else env TQ2_M_SMALL, else 4): M <= threshold
+ * runs the f32 path.  Env TQ2_PATH=f32|mfma forces a path for every auto call. */
+int tq2_select_path(int64_t M);
+
+/* Sets the auto-path threshold (M <= m_small runs on the f32 path); returns the old one. */
+int64_t tq2_set_m_small(int64_t m_small);
+
+/* [TQ2] decode on the GPU: w_out[n][k] = (code-1)*d as f32, device [N][K] row-major,
+ * 16-byte aligned.  Bit-exact with the format's definition (including -0.0 for a
+ * zero code under a negative scale).  Asynchronous on `stream`. */
+int tq2_dequant(const tq2_weight *w, float *w_out, void *stream);
+
+/* Bytes of device workspace blr_forward needs for these sizes (0 on bad sizes). */
+size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/* [BLR] y[t][i] = h[i] * sum_k f16(a[t][k]*l[k]) * S_U[i][k],
+ *        a[t][k] = sum_j f16(x[t][j]*g[j]) * S_V[j][k]          (f32 accumulation).
+ * bits_u: device u32 [d_out][r/32], bits_v: device u32 [d_in][r/32] (the sign
+ * bitmaps, 4-byte aligned); h [d_out], l [r], g [d_in]: device f32; x: device f32
+ * [M][d_in]; y: device f32 [M][d_out], overwritten, 16-byte aligned, must not
+ * overlap the inputs.  Requires d_in >= 1, d_out >= 1, r >= 32, r % 32 == 0, M >= 0
+ * (M == 0 is a no-op).  `workspace` is caller-owned device memory of at least
+ * blr_workspace_size(...) bytes, 256-byte aligned; its contents are scratch.
+ * Preconditions (not checked): |x*g| and |a*l| within f16 range.
+ * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
+int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
+                int64_t r, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *tq2_strerror(int status);
+
+/* Library version string. */
+const char *tq2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBTQ2_H */

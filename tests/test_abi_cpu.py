@@ -1,0 +1,97 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+The shared object must load and export every entry point that include/*.h
+declares; argument errors that the contract says are caught on the host must
+come back as TQ2_EINVAL before any device is touched.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_gemm_amd as bw
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bw.LIB_PATH):
+        from bit_weight_gemm_amd import build
+        build.build()
+    return bw.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for must in ("tq2_upload", "tq2_free", "tq2_gemm", "tq2_gemm_path", "tq2_dequant", "blr_forward",
+                 "blr_workspace_size", "tq2_select_path", "tq2_set_m_small", "tq2_strerror", "tq2_version",
+                 "tq2_weight_info"):
+        assert must in names, must
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_strerror_and_version(L):
+    assert bw.tq2_strerror(0) == "ok"
+    assert "invalid" in bw.tq2_strerror(bw.TQ2_EINVAL)
+    assert bw.tq2_strerror(12345) == "unknown status"
+    assert "gfx950" in bw.tq2_version()
+
+
+def _upload_status(L, aos, nbytes, n, k):
+    out = ctypes.c_void_p()
+    buf = None if aos is None else np.ascontiguousarray(aos, np.uint8)
+    ptr = None if buf is None else buf.ctypes.data_as(ctypes.c_void_p)
+    return L.tq2_upload(ptr, nbytes, n, k, None, ctypes.byref(out)), out
+
+
+def test_upload_rejects_bad_arguments_on_the_host(L):
+    aos, n, k = wl.tiny_weight()
+    assert _upload_status(L, None, aos.size, n, k)[0] == bw.TQ2_EINVAL          # null bytes
+    assert _upload_status(L, aos, aos.size - 1, n, k)[0] == bw.TQ2_EINVAL       # wrong byte count
+    assert _upload_status(L, aos, aos.size, n, 200)[0] == bw.TQ2_EINVAL         # K % 128 != 0
+    assert _upload_status(L, aos, aos.size, 0, k)[0] == bw.TQ2_EINVAL           # N < 1
+    assert _upload_status(L, aos[:0], 0, 1, 0)[0] == bw.TQ2_EINVAL              # K < 128
+    assert L.tq2_upload(aos.ctypes.data_as(ctypes.c_void_p), aos.size, n, k, None, None) == bw.TQ2_EINVAL
+
+
+def test_workspace_size_rules(L):
+    assert bw.blr_workspace_size(512, 4096, 4096, 1024) > 512 * 1024 * 4
+    assert bw.blr_workspace_size(1, 4096, 4096, 1000) == 0     # r % 32 != 0
+    assert bw.blr_workspace_size(1, 0, 4096, 1024) == 0        # d_in < 1
+    assert bw.blr_workspace_size(-1, 8, 8, 32) == 0            # M < 0
+    assert bw.blr_workspace_size(0, 8, 8, 32) > 0              # M == 0 is valid (no-op)
+
+
+def test_auto_path_threshold(L):
+    old = bw.tq2_set_m_small(4)
+    try:
+        assert bw.tq2_select_path(1) == bw.TQ2_PATH_F32
+        assert bw.tq2_select_path(4) == bw.TQ2_PATH_F32
+        assert bw.tq2_select_path(5) == bw.TQ2_PATH_MFMA
+        bw.tq2_set_m_small(0)
+        assert bw.tq2_select_path(1) == bw.TQ2_PATH_MFMA
+    finally:
+        bw.tq2_set_m_small(old)
+
+
+def test_blr_forward_rejects_bad_sizes_on_the_host(L):
+    # r % 32 != 0 is refused before any pointer or device is looked at
+    assert L.blr_forward(None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
