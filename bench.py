@@ -1,0 +1,264 @@
+"""Benchmark of the TQ2_0_g128 ternary GEMM (and the binary low-rank forward) on one MI355X.
+
+Headline: weight-GB/s of tq2_gemm at M=1 (decode GEMV, N=K=4096), i.e. packed
+weight bytes (N*K/128*34) per call over the per-call time, with every call
+reading a different uploaded copy of the weight (more copies than the 256 MB
+Infinity Cache holds, so each call streams from HBM).  The same JSON line also
+reports the M=2048 prefill TFLOP/s, the small-batch MLP up-projection and the
+BLR layer forward, each with its roofline fraction, and the CPU oracle timed on
+this host's cores on a bounded sample.
+
+Timing: W untimed warmup steps, then exactly K steps between two device
+synchronisations.  The K steps are captured once in a HIP graph and replayed, so
+the timed region holds GPU work only (host launch cost removed); HIP events on
+the launch stream bracket the replay.  Each step is one library call.  The same
+K steps issued eagerly from Python are also timed and reported as context.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mlp,blr]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense f16 MFMA
+F32_VALU_PEAK_TFLOPS = 157.3   # fp32 vector
+MALL_BYTES = 256 << 20
+
+
+def tq2_bytes(n, k):
+    return n * (k // 128) * 34
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """W eager warmup steps, then K steps captured in one HIP graph and replayed
+    between two device synchronisations (HIP events on the launch stream bracket
+    the replay).  The graph removes host launch cost from the timed region; every
+    step is still one library call (one or more kernel launches).  The same K
+    steps issued eagerly from Python are timed too, as context."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(warmup):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fn(i)
+        graph.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        region_ms = start.elapsed_time(end)
+        del graph
+        # the same steps issued eagerly (host launch cost included), for context
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return dict(region_ms=region_ms, step_ms=region_ms / steps, host_wall_s=wall,
+                    eager_step_ms=e0.elapsed_time(e1) / steps)
+
+
+def bench_decode(torch, bw, steps, warmup, path):
+    aos, x_np = wl.decode_inputs()
+    n, k = wl.DECODE["N"], wl.DECODE["K"]
+    nbytes = tq2_bytes(n, k)
+    copies = max(2 * MALL_BYTES // nbytes + 1, 8)
+    log(f"[decode] uploading {copies} copies of the {nbytes} B weight")
+    ws = [bw.tq2_upload(aos, n, k) for _ in range(copies)]
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((1, n), device="cuda")
+    t = Timer(torch).run(lambda i: bw.tq2_gemm_path(ws[i % copies], x, y, path), steps, warmup)
+    for w in ws:
+        w.close()
+    t.update(bytes_per_call=nbytes, copies=copies,
+             gbs_step=nbytes / (t["step_ms"] * 1e-3) / 1e9,
+             gbs_eager=nbytes / (t["eager_step_ms"] * 1e-3) / 1e9)
+    return t
+
+
+def bench_prefill(torch, bw, steps, warmup):
+    aos, x_np = wl.prefill_inputs()
+    m, n, k = wl.PREFILL["M"], wl.PREFILL["N"], wl.PREFILL["K"]
+    w = bw.tq2_upload(aos, n, k)
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((m, n), device="cuda")
+    t = Timer(torch).run(lambda i: bw.tq2_gemm_path(w, x, y, bw.TQ2_PATH_MFMA), steps, warmup)
+    w.close()
+    flop = 2.0 * m * n * k
+    t.update(flop_per_call=flop, tflops_step=flop / (t["step_ms"] * 1e-3) / 1e12)
+    return t
+
+
+def bench_mlp(torch, bw, steps, warmup, m, path):
+    aos, x_np = wl.mlp_inputs(m)
+    n, k = wl.MLP["N"], wl.MLP["K"]
+    nbytes = tq2_bytes(n, k)
+    copies = max(2 * MALL_BYTES // nbytes + 1, 4)
+    ws = [bw.tq2_upload(aos, n, k) for _ in range(copies)]
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((m, n), device="cuda")
+    t = Timer(torch).run(lambda i: bw.tq2_gemm_path(ws[i % copies], x, y, path), steps, warmup)
+    for w in ws:
+        w.close()
+    t.update(bytes_per_call=nbytes, copies=copies, gbs_step=nbytes / (t["step_ms"] * 1e-3) / 1e9,
+             tflops_step=2.0 * m * n * k / (t["step_ms"] * 1e-3) / 1e12)
+    return t
+
+
+def bench_blr(torch, bw, steps, warmup):
+    d = wl.blr_inputs()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bu, bv = dev(d["bits_u"].view(np.int32)), dev(d["bits_v"].view(np.int32))
+    h, l, g, x = dev(d["h"]), dev(d["l"]), dev(d["g"]), dev(d["x"])
+    m, d_in = d["x"].shape
+    d_out, r = d["h"].size, d["l"].size
+    y = torch.empty((m, d_out), device="cuda")
+    ws = torch.empty(bw.blr_workspace_size(m, d_in, d_out, r), dtype=torch.uint8, device="cuda")
+    t = Timer(torch).run(lambda i: bw.blr_forward(bu, bv, h, l, g, x, y, ws), steps, warmup)
+    flop = 2.0 * m * r * (d_in + d_out)
+    t.update(flop_per_call=flop, tflops_step=flop / (t["step_ms"] * 1e-3) / 1e12)
+    return t
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the decode workload."""
+    import oracle
+
+    aos, x = wl.decode_inputs()
+    n, k = wl.DECODE["N"], wl.DECODE["K"]
+    # sample: the first `rows` weight rows, repeated until the time budget is spent
+    rows = 512
+    sub = aos[: tq2_bytes(rows, k)]
+    calls, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.gemm(sub, rows, k, x)
+        calls += 1
+    dt = time.perf_counter() - t0
+    gbs = calls * tq2_bytes(rows, k) / dt / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"M=1 decode, first {rows} of {n} weight rows (K={k}), {calls} calls in {dt:.1f} s; "
+                      f"f64 accumulation, OpenMP over outputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--only", default="decode,prefill,mlp,blr,cpu")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the ternary GEMM shards "
+              f"along N with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    only = set(args.only.split(","))
+
+    import torch
+
+    import bit_weight_gemm_amd as bw
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+    K, W = args.steps, args.warmup
+    out = {}
+    if "decode" in only:
+        out["decode_f32"] = bench_decode(torch, bw, K, W, bw.TQ2_PATH_F32)
+        out["decode_mfma"] = bench_decode(torch, bw, max(K // 4, 10), W, bw.TQ2_PATH_MFMA)
+        log(f"[decode] {json.dumps(out['decode_f32'])}")
+    if "prefill" in only:
+        out["prefill"] = bench_prefill(torch, bw, max(K // 20, 20), max(W // 5, 5))
+        log(f"[prefill] {json.dumps(out['prefill'])}")
+    if "mlp" in only:
+        for m in wl.MLP["Ms"]:
+            for name, path in (("f32", bw.TQ2_PATH_F32), ("mfma", bw.TQ2_PATH_MFMA)):
+                out[f"mlp_m{m}_{name}"] = bench_mlp(torch, bw, max(K // 10, 20), max(W // 5, 5), m, path)
+                log(f"[mlp M={m} {name}] {json.dumps(out[f'mlp_m{m}_{name}'])}")
+    if "blr" in only:
+        out["blr"] = bench_blr(torch, bw, max(K // 10, 20), max(W // 5, 5))
+        log(f"[blr] {json.dumps(out['blr'])}")
+
+    line = {
+        "metric": "TQ2 GEMM weight-GB/s (M=1) and TFLOP/s (M=2048), % of HBM/MFMA roofline",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64: codes iid over {-1,0,+1}, f16 scales U(0.01,0.1), x N(0,1))",
+        "config": {"workload": "decode GEMV: tq2_gemm M=1, N=4096, K=4096, TQ2_0_g128 weights "
+                               "(4,456,448 packed bytes per call, rotated over uploaded copies)",
+                   "path": "f32"},
+    }
+    if "decode_f32" in out:
+        d = out["decode_f32"]
+        line["value"] = round(d["gbs_step"], 2)
+        line["ms_per_step"] = d["step_ms"]
+        line["roofline"] = {"bound": "hbm", "achieved": round(d["gbs_step"], 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(d["gbs_step"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "gemv_f32_kernel", "kernel_us": round(d["step_ms"] * 1e3, 3)}
+        line["eager_value"] = round(d["gbs_eager"], 2)
+    if "prefill" in out:
+        p = out["prefill"]
+        line["prefill"] = {"workload": "tq2_gemm M=2048, N=4096, K=4096 (MFMA f16 path, x staged to f16)",
+                           "tflops": round(p["tflops_step"], 2), "ms_per_call": p["step_ms"],
+                           "roofline": {"bound": "mfma", "achieved": round(p["tflops_step"], 2),
+                                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(p["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4),
+                                        "kernel": "mfma_gemm_kernel<128,256>",
+                                        "kernel_us": round(p["step_ms"] * 1e3, 3)}}
+    if "decode_mfma" in out:
+        line["decode_mfma_path"] = {"gbs": round(out["decode_mfma"]["gbs_step"], 2),
+                                    "us_per_call": round(out["decode_mfma"]["step_ms"] * 1e3, 3)}
+    for key in [k for k in out if k.startswith("mlp_")]:
+        v = out[key]
+        line[key] = {"gbs": round(v["gbs_step"], 2), "tflops": round(v["tflops_step"], 3),
+                     "us_per_call": round(v["step_ms"] * 1e3, 3),
+                     "hbm_frac": round(v["gbs_step"] / HBM_PEAK_GBS, 4)}
+    if "blr" in out:
+        b = out["blr"]
+        line["blr"] = {"workload": "blr_forward M=512, d_in=d_out=4096, r=1024 (4 launches per call)",
+                       "tflops": round(b["tflops_step"], 2), "ms_per_call": b["step_ms"],
+                       "mfma_frac": round(b["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4)}
+    if "cpu" in only:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,11 +21,23 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// (q-1) for the pair at position P (0..4) of `w` (codes at bits 2P and 16+2P).
+// The f16 exponent pattern 0x6400 in both halves, materialised in a VGPR behind
+// an asm statement so the compiler cannot fold it: the masked insert below then
+// becomes one v_bfi_b32 (mask in an SGPR, word and pattern in VGPRs) instead of a
+// separate AND and OR.  Call once per kernel and pass the value down.
+__device__ __forceinline__ uint32_t f16_magic() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+    return m;
+}
+
+// (q-1) for the pair at position P (0..4) of `w` (codes at bits 2P and 16+2P):
+// insert the two codes into 0x6400 (f16 1024 + q*4^P), then one packed FMA.
 template <int P>
-__device__ __forceinline__ h2 pair_m1(uint32_t w) {
+__device__ __forceinline__ h2 pair_m1(uint32_t w, uint32_t magic) {
     static_assert(P >= 0 && P <= 4, "pair position must lie in the f16 fraction");
-    const uint32_t t = (w & (0x00030003u << (2 * P))) | 0x64006400u;
+    constexpr uint32_t mask = 0x00030003u << (2 * P);
+    const uint32_t t = (w & mask) | (magic & ~mask);
     constexpr float inv = 1.0f / float(1 << (2 * P));
     constexpr float off = -float((1 << (10 - 2 * P)) + 1);
     const h2 vi = {(_Float16)inv, (_Float16)inv};
@@ -34,24 +46,73 @@ __device__ __forceinline__ h2 pair_m1(uint32_t w) {
 }
 
 // All 8 pairs of a word: out[s] = (q_{2s} - 1, q_{2s+1} - 1).
-__device__ __forceinline__ void word_m1(uint32_t w, h2 out[8]) {
-    out[0] = pair_m1<0>(w);
-    out[1] = pair_m1<1>(w);
-    out[2] = pair_m1<2>(w);
-    out[3] = pair_m1<3>(w);
-    out[4] = pair_m1<4>(w);
+__device__ __forceinline__ void word_m1(uint32_t w, uint32_t magic, h2 out[8]) {
+    out[0] = pair_m1<0>(w, magic);
+    out[1] = pair_m1<1>(w, magic);
+    out[2] = pair_m1<2>(w, magic);
+    out[3] = pair_m1<3>(w, magic);
+    out[4] = pair_m1<4>(w, magic);
     const uint32_t w6 = w >> 6;  // pairs 5,6,7 move to positions 2,3,4
-    out[5] = pair_m1<2>(w6);
-    out[6] = pair_m1<3>(w6);
-    out[7] = pair_m1<4>(w6);
+    out[5] = pair_m1<2>(w6, magic);
+    out[6] = pair_m1<3>(w6, magic);
+    out[7] = pair_m1<4>(w6, magic);
 }
 
 // The 4 pairs of one half-group (elements 8h..8h+7) as an MFMA operand of 8
 // consecutive k: shift the word by 8h so the wanted pairs sit at positions 0..3.
-__device__ __forceinline__ h8 half_group_m1(uint32_t w, int h) {
+__device__ __forceinline__ h8 half_group_m1(uint32_t w, int h, uint32_t magic) {
     const uint32_t ws = w >> (8 * h);
-    const h2 p0 = pair_m1<0>(ws), p1 = pair_m1<1>(ws), p2 = pair_m1<2>(ws), p3 = pair_m1<3>(ws);
+    const h2 p0 = pair_m1<0>(ws, magic), p1 = pair_m1<1>(ws, magic), p2 = pair_m1<2>(ws, magic),
+             p3 = pair_m1<3>(ws, magic);
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+}  // namespace tq2
+
+namespace tq2 {
+
+// ---- cross-lane helpers (wave64)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row; every lane of the row ends with the row's total.
+// Order: xor 1, xor 2 (quad permutes), then rotate by 4 and by 8 within the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x124>(v);  // row_ror:4
+    v += dpp<0x128>(v);  // row_ror:8
+    return v;
+}
+
+// Exchange of lane halves (v_permlane32_swap_b32): returns the pair after the swap.
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                              false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Exchange of odd/even 16-lane rows (v_permlane16_swap_b32).
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                              false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Which operand's row a lane keeps after swap32/swap16 (0: first, 1: second),
+// found by pushing the row tags 0 and 1 through the same exchange.
+__device__ __forceinline__ int kept32() {
+    auto r = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
+    return (int)(uint32_t)r[0];
+}
+__device__ __forceinline__ int kept16() {
+    auto r = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
+    return (int)(uint32_t)r[0];
 }
 
 }  // namespace tq2

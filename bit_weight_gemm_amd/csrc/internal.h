@@ -36,7 +36,7 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
 // Binary low-rank forward.  Workspace carve-up is computed by blr_plan.
 struct BlrPlan {
     int64_t M, d_in, d_out, r;
-    int64_t kpad1, kpad2;        // padded contraction lengths of GEMM1 (d_in) and GEMM2 (r)
+    int64_t kpad1, kpad2;        // contraction lengths of GEMM1 (d_in) and GEMM2 (r), padded to 256
     int64_t npad1, npad2;        // padded output widths of GEMM1 (r) and GEMM2 (d_out)
     size_t off_codes_v, off_codes_u, off_a, total;
 };

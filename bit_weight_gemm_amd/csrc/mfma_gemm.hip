@@ -27,6 +27,7 @@ namespace tq2 {
 
 constexpr int BK = 64;
 
+
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 enum Epi { kEpiStore = 0, kEpiRowScale = 1 };
@@ -43,33 +44,43 @@ struct GemmArgs {
     int64_t ldc;
     const float *rowf;       // [N] output factor (kEpiRowScale)
     int M, N, K;             // true sizes; K bounds the A loads
-    int Kloop;               // K rounded up to a multiple of 64 (codes are padded)
+    int Kloop;               // K rounded up to a multiple of STAGES*64 (codes are padded)
     int tiles_n;             // number of BN tiles along N
-    int a_vec;               // A rows allow 16-byte loads (lda % 4 == 0 and A 16-byte aligned)
+    int a_vec;               // A rows and column factors allow 16-byte loads (K % 4 == 0, aligned)
 };
 
 // 16-byte chunk `kc` (8 halves) of tile row `row`, XOR-swizzled across the row.
 __device__ __forceinline__ int lds_off(int row, int kc) { return row * BK + ((kc ^ (row & 7)) << 3); }
 
-template <int BM, int BN, int WM, int WN, bool KGUARD, bool COLF, bool SCALED, int EPI>
+// AMODE: how A tiles are read.  kAExact: M and K tile exactly or rows past M are
+// clamped (ternary GEMM, K a multiple of 64).  kAVec: 16-byte loads with clamped
+// addresses and zeroing past M and K (needs K % 4 == 0 and 16-byte aligned rows).
+// kAScalar: element-wise guarded loads (any K).
+enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2 };
+
+template <int BM, int BN, int WM, int WN, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
     constexpr int T = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MB = WTM / 32, NB = WTN / 32;
-    constexpr int CHUNKS = BM * (BK / 8);
-    constexpr int CPT = CHUNKS / T;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(CHUNKS % T == 0, "A tile must split evenly over the threads");
 
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * BK];
+    static_assert(STAGES >= 2, "at least two pipeline stages");
+    __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * BK];
+    __shared__ __attribute__((aligned(16))) u4 Bs[STAGES][BN];   // 64 codes (16 B) per B row and step
+    __shared__ _Float16 Ds[STAGES][BN];                          // B row scale for the step
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
     const int lrow = lane & 31, hk = lane >> 5;
+    const uint32_t magic = f16_magic();
 
-    // Tile order: consecutive workgroups walk N first, so the ones sharing an A
-    // row-block run together and reuse it from L2.
-    const int tile = blockIdx.x;
+    // Tile order: the hardware deals workgroups round-robin to the 8 XCDs; remap
+    // so each XCD gets a contiguous run of tiles, and within the run walk N
+    // first, so the workgroups sharing an A row-block share one XCD's L2.
+    const int tiles = gridDim.x;
+    int tile = blockIdx.x;
+    if ((tiles & 7) == 0) tile = (tile & 7) * (tiles >> 3) + (tile >> 3);
     const int m0 = (tile / p.tiles_n) * BM;
     const int n0 = (tile % p.tiles_n) * BN;
 
@@ -79,71 +90,101 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f16x{};
 
-    // ---- prefetch registers
-    float areg[CPT][8];
-    u4 breg[NB];
-    _Float16 dreg[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) dreg[nb] = (_Float16)1.0f;
+    // Two register stages of prefetch: the loads for step k+2 are issued while
+    // step k computes, so each global load has two compute phases to land.  Every
+    // loaded value (A as f16, B code words and scales) goes through LDS, so a
+    // stage's registers are free again right after the LDS store at the top of
+    // its step.
+    constexpr int BPT = (BN + T - 1) / T;  // B rows loaded per thread
+    // A is moved in 16-byte pieces (4 floats): piece q of tile row r covers
+    // k = 4q..4q+3; consecutive lanes take consecutive pieces of a row, so each
+    // wave-wide load reads whole 256-byte row segments.
+    constexpr int PIECES = BM * (BK / 4);
+    constexpr int PPT = PIECES / T;
+    static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
+    f4 areg[STAGES][PPT];
+    f4 creg[STAGES][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
+    u4 breg[STAGES][BPT];
+    uint16_t dreg[STAGES][BPT];
 
-    auto load_a = [&](int k0) {
+    auto load_a = [&](int st, int k0) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int chunk = tid + c * T;
-            const int row = chunk >> 3, kc = chunk & 7;
-            const int gm = m0 + row, gk = k0 + kc * 8;
-            if (gm < p.M && (!KGUARD || (p.a_vec && gk + 8 <= p.K))) {
-                const f4 *src = reinterpret_cast<const f4 *>(p.A + (int64_t)gm * p.lda + gk);
-                const f4 v0 = src[0], v1 = src[1];
-                areg[c][0] = v0.x, areg[c][1] = v0.y, areg[c][2] = v0.z, areg[c][3] = v0.w;
-                areg[c][4] = v1.x, areg[c][5] = v1.y, areg[c][6] = v1.z, areg[c][7] = v1.w;
+        for (int c = 0; c < PPT; ++c) {
+            const int piece = tid + c * T;
+            const int row = piece >> 4, q = piece & 15;
+            const int gm = m0 + row, gk = k0 + q * 4;
+            // rows past M read row M-1 (valid memory); store() zeroes them
+            const int gmc = gm < p.M ? gm : p.M - 1;
+            if constexpr (AMODE == kAExact) {
+                areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
+                if constexpr (COLF) creg[st][c] = *reinterpret_cast<const f4 *>(p.colf + gk);
+            } else if constexpr (AMODE == kAVec) {
+                // K % 4 == 0: a piece is wholly inside or wholly past K
+                const bool in = gk < p.K;
+                const int gkc = in ? gk : 0;
+                const f4 v = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gkc);
+                areg[st][c] = in ? v : f4{};
+                if constexpr (COLF) {
+                    const f4 cf = *reinterpret_cast<const f4 *>(p.colf + gkc);
+                    creg[st][c] = in ? cf : f4{};
+                }
             } else {
+                f4 v, cf;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    areg[c][e] = (gm < p.M && KGUARD && gk + e < p.K) ? p.A[(int64_t)gm * p.lda + gk + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    const bool in = gk + e < p.K;
+                    v[e] = (gm < p.M && in) ? p.A[(int64_t)gm * p.lda + gk + e] : 0.0f;
+                    cf[e] = (COLF && in) ? p.colf[gk + e] : 0.0f;
+                }
+                areg[st][c] = v;
+                if constexpr (COLF) creg[st][c] = cf;
             }
         }
     };
-    auto load_b = [&](int k0) {
+    auto load_b = [&](int st, int k0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int64_t n = n0 + wn * WTN + nb * 32 + lrow;
-            breg[nb] = *reinterpret_cast<const u4 *>(p.codes + n * p.kw + (k0 >> 4));
-            if constexpr (SCALED) dreg[nb] = __builtin_bit_cast(_Float16, p.scales[n * p.kbw + k0 / kBlock]);
+        for (int i = 0; i < BPT; ++i) {
+            const int row = tid + i * T;
+            if (BN % T == 0 || row < BN) {
+                const int64_t n = n0 + row;
+                breg[st][i] = *reinterpret_cast<const u4 *>(p.codes + n * p.kw + (k0 >> 4));
+                if constexpr (SCALED) dreg[st][i] = p.scales[n * p.kbw + k0 / kBlock];
+            }
         }
     };
-    auto store_a = [&](int buf, int k0) {
+    auto store = [&](int st, int k0) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int chunk = tid + c * T;
-            const int row = chunk >> 3, kc = chunk & 7;
-            h8 v;
+        for (int c = 0; c < PPT; ++c) {
+            const int piece = tid + c * T;
+            const int row = piece >> 4, q = piece & 15;
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            h4 v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = areg[c][e];
-                if constexpr (COLF) {
-                    const int gk = k0 + kc * 8 + e;
-                    a = (!KGUARD || gk < p.K) ? a * p.colf[gk] : 0.0f;
-                }
+            for (int e = 0; e < 4; ++e) {
+                float a = areg[st][c][e];
+                if constexpr (COLF) a = a * creg[st][c][e];  // factors past K are 0
                 v[e] = (_Float16)a;
             }
-            *reinterpret_cast<h8 *>(&As[buf][lds_off(row, kc)]) = v;
+            if (AMODE != kAScalar && m0 + row >= p.M) v = h4{};  // clamped rows past M contribute zero
+            *reinterpret_cast<h4 *>(&As[st][lds_off(row, q >> 1) + ((q & 1) << 2)]) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int row = tid + i * T;
+            if (BN % T == 0 || row < BN) {
+                Bs[st][row] = breg[st][i];
+                if constexpr (SCALED) Ds[st][row] = __builtin_bit_cast(_Float16, dreg[st][i]);
+            }
         }
     };
-
-    load_a(0);
-    load_b(0);
-    int buf = 0;
-    for (int k0 = 0; k0 < p.Kloop; k0 += BK, buf ^= 1) {
-        store_a(buf, k0);
-        u4 bcur[NB];
-        _Float16 dcur[NB];
+    auto compute = [&](int st) {
+        u4 bw[NB];
+        _Float16 dv[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bcur[nb] = breg[nb], dcur[nb] = dreg[nb];
-        __syncthreads();
-        if (k0 + BK < p.Kloop) {
-            load_a(k0 + BK);
-            load_b(k0 + BK);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = wn * WTN + nb * 32 + lrow;
+            bw[nb] = Bs[st][row];
+            dv[nb] = SCALED ? Ds[st][row] : (_Float16)1.0f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -151,12 +192,12 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = wm * WTM + mb * 32 + lrow;
-                a[mb] = *reinterpret_cast<const h8 *>(&As[buf][lds_off(row, 2 * j + hk)]);
+                a[mb] = *reinterpret_cast<const h8 *>(&As[st][lds_off(row, 2 * j + hk)]);
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                b[nb] = half_group_m1(bcur[nb][j], hk);
-                if constexpr (SCALED) b[nb] = b[nb] * dcur[nb];
+                b[nb] = half_group_m1(bw[nb][j], hk, magic);
+                if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -164,6 +205,36 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
                 for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
         }
+    };
+    // One pipeline step on stage/buffer st: registers -> LDS, barrier, refill the
+    // registers with step k0 + STAGES*BK, compute from LDS.  Buffer st is
+    // rewritten STAGES steps later, after every wave has passed the barriers of
+    // the steps in between, i.e. finished reading it.  Kloop is a multiple of
+    // STAGES*BK, so the loop body is branch-free; refills past the end re-read
+    // the last step (clamped address) and are never used.
+    auto step = [&](int st, int k0) {
+        store(st, k0);
+        __syncthreads();
+        const int kn = (k0 + STAGES * BK < p.Kloop) ? k0 + STAGES * BK : p.Kloop - BK;
+        load_a(st, kn);
+        load_b(st, kn);
+        // keep the refill loads ahead of the MFMAs (the scheduler would otherwise
+        // sink them below the compute and shorten the prefetch distance)
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st);
+    };
+
+    // Prologue in stage order (the loop's wait counts assume lower stages hold
+    // the older loads), then the pipelined loop.
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) {
+        load_a(st, st * BK);
+        load_b(st, st * BK);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int k0 = 0; k0 < p.Kloop; k0 += STAGES * BK) {
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) step(st, k0 + st * BK);
     }
 
     // ---- epilogue: lane holds column lrow, rows 8*(r/4) + 4*hk + r%4 of each block
@@ -185,13 +256,13 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
         }
 }
 
-template <int BM, int BN, int WM, int WN, bool KGUARD, bool COLF, bool SCALED, int EPI>
+template <int BM, int BN, int WM, int WN, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI>
 static hipError_t run_gemm(GemmArgs p, int64_t npad, hipStream_t s) {
     p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= npad, so B rows stay in bounds
     (void)npad;
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
-    mfma_gemm_kernel<BM, BN, WM, WN, KGUARD, COLF, SCALED, EPI>
+    mfma_gemm_kernel<BM, BN, WM, WN, STAGES, AMODE, COLF, SCALED, EPI>
         <<<dim3((unsigned)tiles), dim3(WM * WN * 64), 0, s>>>(p);
     return hipGetLastError();
 }
@@ -215,8 +286,13 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     p.K = (int)w.K;
     p.Kloop = (int)w.K;
     p.a_vec = 1;
-    if (M <= 64) return run_gemm<32, 256, 1, 4, false, false, true, kEpiStore>(p, w.Npad, s);
-    return run_gemm<128, 256, 1, 4, false, false, true, kEpiStore>(p, w.Npad, s);
+    // K is a multiple of 128 (two steps); four stages when the step count allows
+    const bool four = (w.K / BK) % 4 == 0;
+    if (M <= 64)
+        return four ? run_gemm<32, 256, 1, 4, 4, kAExact, false, true, kEpiStore>(p, w.Npad, s)
+                    : run_gemm<32, 256, 1, 4, 2, kAExact, false, true, kEpiStore>(p, w.Npad, s);
+    return four ? run_gemm<128, 256, 1, 4, 4, kAExact, false, true, kEpiStore>(p, w.Npad, s)
+                : run_gemm<128, 256, 1, 4, 2, kAExact, false, true, kEpiStore>(p, w.Npad, s);
 }
 
 // ------------------------------------------------------------------ binary low-rank forward
@@ -228,8 +304,8 @@ constexpr int kBlrBN = 64;
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrPlan p{};
     p.M = M, p.d_in = d_in, p.d_out = d_out, p.r = r;
-    p.kpad1 = round_up(d_in, BK);
-    p.kpad2 = round_up(r, BK);
+    p.kpad1 = round_up(d_in, 4 * BK);  // four pipeline stages of BK
+    p.kpad2 = round_up(r, 4 * BK);
     p.npad1 = round_up(r, kRowPad);
     p.npad2 = round_up(d_out, kRowPad);
     size_t off = 0;
@@ -248,26 +324,43 @@ BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 // Sign bitmaps -> code words (set bit -> code 2 = +1, clear -> code 0 = -1,
 // padding -> code 1 = 0) in the device layout, with row index `n` and
 // contraction index `k`:
-//   TRANS = false: sign(n, k) = bit k of bits[n][k/32]   (S_U: n = output i, k = rank)
-//   TRANS = true:  sign(n, k) = bit n of bits[k][n/32]   (S_V: n = rank, k = input j)
-template <bool TRANS>
-__global__ __launch_bounds__(256) void bits_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
-                                                            uint32_t *__restrict__ codes, int64_t n_real,
-                                                            int64_t k_real, int64_t n_pad, int64_t k_pad) {
+//   S_U: sign(n, k) = bit k of bits[n][k/32]   (n = output i, k = rank): one
+//        thread per output word, reading half a bitmap word;
+//   S_V: sign(n, k) = bit n of bits[k][n/32]   (n = rank, k = input j): a wave
+//        covers 64 consecutive ranks of one 16-wide k group, so each of its 16
+//        loads touches two bitmap words shared by all lanes.
+__global__ __launch_bounds__(256) void bits_u_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
+                                                              uint32_t *__restrict__ codes, int64_t n_real,
+                                                              int64_t k_real, int64_t n_pad, int64_t k_pad) {
     const int64_t kw = k_pad / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= n_pad * kw) return;
     const int64_t n = gid / kw, g = gid % kw;
+    uint32_t half = 0;
+    if (n < n_real && g * 16 < k_real) half = (bits[n * words + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu;
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int64_t k = g * 16 + e;
+        const uint32_t code = (n < n_real && k < k_real) ? (((half >> e) & 1u) ? 2u : 0u) : 1u;
+        out |= code << (2 * (e >> 1) + 16 * (e & 1));
+    }
+    codes[n * kw + g] = out;
+}
+
+__global__ __launch_bounds__(256) void bits_v_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
+                                                              uint32_t *__restrict__ codes, int64_t n_real,
+                                                              int64_t k_real, int64_t n_pad, int64_t k_pad) {
+    const int64_t kw = k_pad / 16;
+    const int64_t n = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const int64_t g = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (n >= n_pad || g >= kw) return;
     uint32_t out = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int64_t k = g * 16 + e;
         uint32_t code = 1;
-        if (n < n_real && k < k_real) {
-            const uint32_t b = TRANS ? (bits[k * words + (n >> 5)] >> (n & 31)) & 1u
-                                     : (bits[n * words + (k >> 5)] >> (k & 31)) & 1u;
-            code = b ? 2u : 0u;
-        }
+        if (n < n_real && k < k_real) code = ((bits[k * words + (n >> 5)] >> (n & 31)) & 1u) ? 2u : 0u;
         out |= code << (2 * (e >> 1) + 16 * (e & 1));
     }
     codes[n * kw + g] = out;
@@ -283,11 +376,10 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     const int64_t words = pl.r / 32;
 
     {
-        const int64_t tot = pl.npad1 * (pl.kpad1 / 16);
-        bits_to_codes_kernel<true><<<dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s>>>(
-            bits_v, words, codes_v, pl.r, pl.d_in, pl.npad1, pl.kpad1);
+        const dim3 gv((unsigned)(pl.npad1 / 64), (unsigned)((pl.kpad1 / 16 + 3) / 4));
+        bits_v_to_codes_kernel<<<gv, dim3(256), 0, s>>>(bits_v, words, codes_v, pl.r, pl.d_in, pl.npad1, pl.kpad1);
         const int64_t tot2 = pl.npad2 * (pl.kpad2 / 16);
-        bits_to_codes_kernel<false><<<dim3((unsigned)((tot2 + 255) / 256)), dim3(256), 0, s>>>(
+        bits_u_to_codes_kernel<<<dim3((unsigned)((tot2 + 255) / 256)), dim3(256), 0, s>>>(
             bits_u, words, codes_u, pl.d_out, pl.r, pl.npad2, pl.kpad2);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -298,8 +390,10 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p1.codes = codes_v, p1.kw = pl.kpad1 / 16, p1.scales = nullptr, p1.kbw = 0;
     p1.C = a, p1.ldc = pl.r, p1.rowf = nullptr;
     p1.M = (int)pl.M, p1.N = (int)pl.r, p1.K = (int)pl.d_in, p1.Kloop = (int)pl.kpad1;
-    p1.a_vec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-    hipError_t e = run_gemm<64, kBlrBN, 2, 2, true, true, false, kEpiStore>(p1, pl.npad1, s);
+    p1.a_vec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+               ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+    hipError_t e = p1.a_vec ? run_gemm<64, kBlrBN, 2, 2, 4, kAVec, true, false, kEpiStore>(p1, pl.npad1, s)
+                            : run_gemm<64, kBlrBN, 2, 2, 4, kAScalar, true, false, kEpiStore>(p1, pl.npad1, s);
     if (e != hipSuccess) return e;
     // GEMM2: y[M][d_out] = h . (f16(a.l) . S_U^T)
     GemmArgs p2{};
@@ -307,8 +401,10 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p2.codes = codes_u, p2.kw = pl.kpad2 / 16, p2.scales = nullptr, p2.kbw = 0;
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
     p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.r, p2.Kloop = (int)pl.kpad2;
-    p2.a_vec = 1;
-    return run_gemm<64, kBlrBN, 2, 2, true, true, false, kEpiRowScale>(p2, pl.npad2, s);
+    // a is the 256-byte aligned workspace and r % 32 == 0; l decides
+    p2.a_vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
+    return p2.a_vec ? run_gemm<64, kBlrBN, 2, 2, 4, kAVec, true, false, kEpiRowScale>(p2, pl.npad2, s)
+                    : run_gemm<64, kBlrBN, 2, 2, 4, kAScalar, true, false, kEpiRowScale>(p2, pl.npad2, s);
 }
 
 }  // namespace tq2

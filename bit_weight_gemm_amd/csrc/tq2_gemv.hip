@@ -8,7 +8,13 @@
 #include "decode.h"
 #include "internal.h"
 
+#ifndef TQ2_GEMV_ROWS_M1
+#define TQ2_GEMV_ROWS_M1 16
+#endif
+
 namespace tq2 {
+
+constexpr int kGemvRowsM1 = TQ2_GEMV_ROWS_M1;  // weight rows per workgroup at M = 1
 
 // ------------------------------------------------------------------ decode
 
@@ -42,29 +48,34 @@ hipError_t launch_dequant(const DevWeight &w, float *out, hipStream_t s) {
 
 // ------------------------------------------------------------------ f32 small-M product
 //
-// Work split: a workgroup of 4 waves owns RW = 16 weight rows and MT activation
-// rows.  K is walked in passes of 4096: wave w takes elements [1024w, 1024w+1024)
-// of the pass and lane l the 16-element group l of that range, so one wave-wide
-// load reads 256 contiguous bytes of a row.  Each lane keeps its 16 x values per
+// Work split: a workgroup of 4 waves owns RW weight rows and MT activation rows.
+// K is walked in passes of 4096: wave w takes elements [1024w, 1024w+1024) of
+// the pass and lane l the 16-element group l of that range, so one wave-wide load
+// reads 256 contiguous bytes of a row.  Each lane keeps its 16 x values per
 // activation row in registers and, for each weight row, decodes the group word
 // into 8 exact f16 pairs of (q - 1) and accumulates x*(q-1) with mixed
-// f32 x f16 -> f32 fused multiply-adds (16 terms, one block), scales the partial by
-// the block's d, and keeps a per-lane running sum.  The lane sums are reduced
-// across the wave with cross-lane adds, then across the 4 waves through LDS.
-// All additions happen in a fixed order, so results are bitwise reproducible.
-constexpr int kGemvRows = 16;
-
-template <int MT>
+// f32 x f16 -> f32 fused multiply-adds (16 terms of one block), scales the partial
+// by the block's d and keeps a per-lane running sum.
+//
+// Reduction of the RW lane sums over the wave without LDS: a lane-half exchange
+// (v_permlane32_swap) adds rows r and r+RW/2 pairwise so each half of the wave
+// keeps half the rows, a 16-lane-row exchange (v_permlane16_swap) halves them
+// again, and DPP adds finish each 16-lane row; every row's wave sum then sits in
+// one lane per 16-lane row.  The 4 waves are added through LDS.  The order of all
+// additions is fixed, so results are bitwise reproducible.
+template <int RW, int MT>
 __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restrict__ codes,
                                                        const uint16_t *__restrict__ scales,
                                                        const float *__restrict__ x, float *__restrict__ y,
                                                        int M, int N, int K) {
-    constexpr int RW = kGemvRows;
+    static_assert(RW == 4 || RW == 8 || RW == 16, "rows per workgroup");
+    constexpr int H1 = RW / 2, H2 = RW / 4;
     __shared__ float red[4][RW][MT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * RW;
     const int m0 = blockIdx.y * MT;
     const int kw = K >> 4, kb = K / kBlock;
+    const uint32_t magic = f16_magic();
 
     float acc[RW][MT];
 #pragma unroll
@@ -75,32 +86,40 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
     for (int kp = 0; kp < K; kp += 4096) {
         const int g = (kp >> 4) + wave * 64 + lane;  // group index within the row
         if (g < kw) {
-            float xv[MT][16];
+            // Issue every load of this pass before any arithmetic, so the whole
+            // pass costs one memory round trip.
+            uint32_t cw[RW];
+            uint16_t db[RW];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) cw[r] = codes[(int64_t)(n0 + r) * kw + g];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) db[r] = scales[(int64_t)(n0 + r) * kb + (g >> 3)];
+            f4 xr[MT][4];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                if (m0 + t < M) {
-                    const f4 *xp = reinterpret_cast<const f4 *>(x + (int64_t)(m0 + t) * K + g * 16);
+                const f4 *xp = reinterpret_cast<const f4 *>(x + (int64_t)(m0 + t < M ? m0 + t : m0) * K + g * 16);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const f4 v = xp[i];
-                        xv[t][4 * i] = v.x, xv[t][4 * i + 1] = v.y, xv[t][4 * i + 2] = v.z, xv[t][4 * i + 3] = v.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) xv[t][e] = 0.0f;
-                }
+                for (int i = 0; i < 4; ++i) xr[t][i] = xp[i];
             }
-            uint32_t cw[RW];
+            __builtin_amdgcn_sched_barrier(0);
             float d[RW];
 #pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                cw[r] = codes[(int64_t)(n0 + r) * kw + g];
-                d[r] = (float)__builtin_bit_cast(_Float16, scales[(int64_t)(n0 + r) * kb + (g >> 3)]);
-            }
+            for (int r = 0; r < RW; ++r) d[r] = (float)__builtin_bit_cast(_Float16, db[r]);
+            float xv[MT][16];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool live = m0 + t < M;
+                    xv[t][4 * i] = live ? xr[t][i].x : 0.0f;
+                    xv[t][4 * i + 1] = live ? xr[t][i].y : 0.0f;
+                    xv[t][4 * i + 2] = live ? xr[t][i].z : 0.0f;
+                    xv[t][4 * i + 3] = live ? xr[t][i].w : 0.0f;
+                }
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
                 h2 p[8];
-                word_m1(cw[r], p);
+                word_m1(cw[r], magic, p);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     float s = 0.0f;
@@ -115,15 +134,24 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
         }
     }
 
+    const int k32 = kept32(), k16 = kept16();
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int t = 0; t < MT; ++t) {
+        float s1[H1];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            float v = acc[r][t];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-            if (lane == 0) red[wave][r][t] = v;
+        for (int r = 0; r < H1; ++r) {
+            float a = acc[r][t], b = acc[r + H1][t];
+            swap32(a, b);
+            s1[r] = a + b;  // row r + H1*k32
         }
+#pragma unroll
+        for (int r = 0; r < H2; ++r) {
+            float a = s1[r], b = s1[r + H2];
+            swap16(a, b);
+            const float v = row16_sum(a + b);  // row r + H2*k16 + H1*k32
+            if ((lane & 15) == 0) red[wave][r + H2 * k16 + H1 * k32][t] = v;
+        }
+    }
     __syncthreads();
     if (threadIdx.x < RW * MT) {
         const int r = threadIdx.x / MT, t = threadIdx.x % MT;
@@ -132,27 +160,26 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
     }
 }
 
-hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s) {
-    const unsigned gx = (unsigned)(w.Npad / kGemvRows);
-    if (M == 1) {
-        gemv_f32_kernel<1><<<dim3(gx, 1), dim3(256), 0, s>>>(w.codes, w.scales, x, y, 1, (int)w.N, (int)w.K);
-        return hipGetLastError();
-    }
-    if (M == 2) {
-        gemv_f32_kernel<2><<<dim3(gx, 1), dim3(256), 0, s>>>(w.codes, w.scales, x, y, 2, (int)w.N, (int)w.K);
-        return hipGetLastError();
-    }
-    // grid.y is limited to 65535 row tiles of 4; larger M runs in slices.
-    const int64_t slice = 65535 * 4;
+template <int RW, int MT>
+static hipError_t gemv_launch(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s) {
+    const unsigned gx = (unsigned)(w.Npad / RW);
+    // grid.y is limited to 65535 row tiles; larger M runs in slices.
+    const int64_t slice = (int64_t)65535 * MT;
     for (int64_t m0 = 0; m0 < M; m0 += slice) {
         const int64_t mm = (M - m0 < slice) ? (M - m0) : slice;
-        const unsigned gy = (unsigned)((mm + 3) / 4);
-        gemv_f32_kernel<4><<<dim3(gx, gy), dim3(256), 0, s>>>(w.codes, w.scales, x + m0 * w.K, y + m0 * w.N,
-                                                              (int)mm, (int)w.N, (int)w.K);
+        const unsigned gy = (unsigned)((mm + MT - 1) / MT);
+        gemv_f32_kernel<RW, MT><<<dim3(gx, gy), dim3(256), 0, s>>>(w.codes, w.scales, x + m0 * w.K, y + m0 * w.N,
+                                                                  (int)mm, (int)w.N, (int)w.K);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s) {
+    if (M == 1) return gemv_launch<kGemvRowsM1, 1>(w, x, y, M, s);
+    if (M == 2) return gemv_launch<8, 2>(w, x, y, M, s);
+    return gemv_launch<8, 4>(w, x, y, M, s);
 }
 
 }  // namespace tq2
