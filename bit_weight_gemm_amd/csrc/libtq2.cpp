@@ -156,15 +156,15 @@ int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *strea
             for (int g = 0; g < 8; ++g) {
                 const uint32_t wv = group_word(blk + 4 * g);
                 has3 |= ((wv & (wv >> 1)) & 0x55555555u) != 0;
-                hc[n * kw + b * 8 + g] = wv;
+                hc[tq2::code_index(n, b * 8 + g, kw)] = wv;
             }
             // |2d| must stay within f16 for the MFMA operand (code 3 = +2d).
             if (has3 && (d & 0x7fff) > 0x77ff) mfma_ok = false;
-            hs[n * kb + b] = d;
+            hs[tq2::scale_index(n, b, kb)] = d;
         }
     }
     for (int64_t n = N; n < npad; ++n)
-        for (int64_t g = 0; g < kw; ++g) hc[n * kw + g] = 0x55555555u;  // code 1 = weight 0
+        for (int64_t g = 0; g < kw; ++g) hc[tq2::code_index(n, g, kw)] = 0x55555555u;  // code 1 = weight 0
 
     tq2_weight *w = new (std::nothrow) tq2_weight;
     if (!w) return TQ2_ENOMEM;

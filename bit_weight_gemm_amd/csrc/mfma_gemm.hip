@@ -67,8 +67,8 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 
     static_assert(STAGES >= 2, "at least two pipeline stages");
     __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * BK];
-    __shared__ __attribute__((aligned(16))) u4 Bs[STAGES][BN];   // 64 codes (16 B) per B row and step
-    __shared__ _Float16 Ds[STAGES][BN];                          // B row scale for the step
+    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][BN * 4];  // 4 code words (64 k) per B row
+    __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][BN];      // B row scale for the step
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
@@ -95,7 +95,9 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
     // loaded value (A as f16, B code words and scales) goes through LDS, so a
     // stage's registers are free again right after the LDS store at the top of
     // its step.
-    constexpr int BPT = (BN + T - 1) / T;  // B rows loaded per thread
+    // B arrives in 16-byte units holding one 16-element group of four rows; a
+    // step needs BN units (BN/4 row quads x 4 groups), BPT per thread.
+    constexpr int BPT = (BN + T - 1) / T;
     // A is moved in 16-byte pieces (4 floats): piece q of tile row r covers
     // k = 4q..4q+3; consecutive lanes take consecutive pieces of a row, so each
     // wave-wide load reads whole 256-byte row segments.
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
     f4 areg[STAGES][PPT];
     f4 creg[STAGES][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
     u4 breg[STAGES][BPT];
-    uint16_t dreg[STAGES][BPT];
+    uint2 dreg[STAGES];  // scales of one row quad (threads tid < BN/4)
 
     auto load_a = [&](int st, int k0) {
 #pragma unroll
@@ -142,13 +144,19 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
         }
     };
     auto load_b = [&](int st, int k0) {
+        const u4 *c4 = reinterpret_cast<const u4 *>(p.codes);
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int row = tid + i * T;
-            if (BN % T == 0 || row < BN) {
-                const int64_t n = n0 + row;
-                breg[st][i] = *reinterpret_cast<const u4 *>(p.codes + n * p.kw + (k0 >> 4));
-                if constexpr (SCALED) dreg[st][i] = p.scales[n * p.kbw + k0 / kBlock];
+            const int item = tid + i * T;
+            if (BN % T == 0 || item < BN) {
+                const int64_t quad = (n0 >> 2) + (item >> 2);
+                breg[st][i] = c4[quad * p.kw + (k0 >> 4) + (item & 3)];
+            }
+        }
+        if constexpr (SCALED) {
+            if (tid < BN / 4) {
+                const uint2 *s4 = reinterpret_cast<const uint2 *>(p.scales);
+                dreg[st] = s4[((n0 >> 2) + tid) * p.kbw + k0 / kBlock];
             }
         }
     };
@@ -170,20 +178,28 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int row = tid + i * T;
-            if (BN % T == 0 || row < BN) {
-                Bs[st][row] = breg[st][i];
-                if constexpr (SCALED) Ds[st][row] = __builtin_bit_cast(_Float16, dreg[st][i]);
+            const int item = tid + i * T;
+            if (BN % T == 0 || item < BN) {
+                const int r0 = (item >> 2) * 4, g = item & 3;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Bs[st][(r0 + r) * 4 + g] = breg[st][i][r];
             }
         }
+        if constexpr (SCALED) {
+            if (tid < BN / 4) *reinterpret_cast<uint2 *>(&Ds[st][4 * tid]) = dreg[st];
+        }
     };
-    auto compute = [&](int st) {
+
+    // compute(st, hook): the MFMAs of the step in LDS buffer st; hook() runs after
+    // the first 16-wide sub-step, so the staging of the next step overlaps the
+    // remaining MFMAs of this one.
+    auto compute = [&](int st, auto &&hook) {
         u4 bw[NB];
         _Float16 dv[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int row = wn * WTN + nb * 32 + lrow;
-            bw[nb] = Bs[st][row];
+            bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][row * 4]);
             dv[nb] = SCALED ? Ds[st][row] : (_Float16)1.0f;
         }
 #pragma unroll
@@ -204,37 +220,45 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+            if (j == 0) hook();
         }
     };
-    // One pipeline step on stage/buffer st: registers -> LDS, barrier, refill the
-    // registers with step k0 + STAGES*BK, compute from LDS.  Buffer st is
-    // rewritten STAGES steps later, after every wave has passed the barriers of
-    // the steps in between, i.e. finished reading it.  Kloop is a multiple of
-    // STAGES*BK, so the loop body is branch-free; refills past the end re-read
-    // the last step (clamped address) and are never used.
-    auto step = [&](int st, int k0) {
-        store(st, k0);
-        __syncthreads();
-        const int kn = (k0 + STAGES * BK < p.Kloop) ? k0 + STAGES * BK : p.Kloop - BK;
-        load_a(st, kn);
-        load_b(st, kn);
-        // keep the refill loads ahead of the MFMAs (the scheduler would otherwise
-        // sink them below the compute and shorten the prefetch distance)
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st);
-    };
 
-    // Prologue in stage order (the loop's wait counts assume lower stages hold
-    // the older loads), then the pipelined loop.
+    // Pipeline: register stages hold steps loaded from memory but not yet in LDS;
+    // LDS buffer t % STAGES holds step t.  While step t computes, step t+1 moves
+    // from registers to LDS and its register stage is refilled with step
+    // t+1+STAGES (loads issued STAGES steps before they are stored).  One
+    // barrier per step makes step t+1's tile visible; buffer (t+1) % STAGES was
+    // last read by step t+1-STAGES <= t-1, which every wave finished before the
+    // barrier that ended step t-1.  Kloop is a multiple of STAGES*BK, so the loop
+    // is branch-free; loads and stores past the end use clamped addresses and
+    // are never read.
+    const int nsteps = p.Kloop / BK;
+    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * BK; };
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) {
         load_a(st, st * BK);
         load_b(st, st * BK);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int k0 = 0; k0 < p.Kloop; k0 += STAGES * BK) {
+    store(0, 0);
+    load_a(0, clampk(STAGES));
+    load_b(0, clampk(STAGES));
+    __syncthreads();
+    for (int t0 = 0; t0 < nsteps; t0 += STAGES) {
 #pragma unroll
-        for (int st = 0; st < STAGES; ++st) step(st, k0 + st * BK);
+        for (int s = 0; s < STAGES; ++s) {
+            const int t = t0 + s;
+            constexpr int dummy = 0;
+            (void)dummy;
+            const int nx = (s + 1) % STAGES;  // register stage and LDS buffer of step t+1
+            compute(s, [&] {
+                store(nx, clampk(t + 1));
+                load_a(nx, clampk(t + 1 + STAGES));
+                load_b(nx, clampk(t + 1 + STAGES));
+            });
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane holds column lrow, rows 8*(r/4) + 4*hk + r%4 of each block
@@ -335,7 +359,7 @@ __global__ __launch_bounds__(256) void bits_u_to_codes_kernel(const uint32_t *__
     const int64_t kw = k_pad / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= n_pad * kw) return;
-    const int64_t n = gid / kw, g = gid % kw;
+    const int64_t n = gid / kw, g = gid % kw;  // reads along the bitmap row
     uint32_t half = 0;
     if (n < n_real && g * 16 < k_real) half = (bits[n * words + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu;
     uint32_t out = 0;
@@ -345,7 +369,7 @@ __global__ __launch_bounds__(256) void bits_u_to_codes_kernel(const uint32_t *__
         const uint32_t code = (n < n_real && k < k_real) ? (((half >> e) & 1u) ? 2u : 0u) : 1u;
         out |= code << (2 * (e >> 1) + 16 * (e & 1));
     }
-    codes[n * kw + g] = out;
+    codes[code_index(n, g, kw)] = out;
 }
 
 __global__ __launch_bounds__(256) void bits_v_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
@@ -363,7 +387,7 @@ __global__ __launch_bounds__(256) void bits_v_to_codes_kernel(const uint32_t *__
         if (n < n_real && k < k_real) code = ((bits[k * words + (n >> 5)] >> (n & 31)) & 1u) ? 2u : 0u;
         out |= code << (2 * (e >> 1) + 16 * (e & 1));
     }
-    codes[n * kw + g] = out;
+    codes[code_index(n, g, kw)] = out;
 }
 
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,

@@ -8,13 +8,16 @@
 #include "decode.h"
 #include "internal.h"
 
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
 #ifndef TQ2_GEMV_ROWS_M1
-#define TQ2_GEMV_ROWS_M1 16
+#define TQ2_GEMV_ROWS_M1 4
 #endif
 
 namespace tq2 {
 
-constexpr int kGemvRowsM1 = TQ2_GEMV_ROWS_M1;  // weight rows per workgroup at M = 1
+constexpr int kGemvRowsM1 = TQ2_GEMV_ROWS_M1;
+static_assert(kGemvRowsM1 % 4 == 0, "rows per workgroup come in groups of four");  // weight rows per workgroup at M = 1
 
 // ------------------------------------------------------------------ decode
 
@@ -26,8 +29,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= N * kw) return;
     const int64_t n = gid / kw, g = gid % kw;
-    const uint32_t w = codes[n * kw + g];
-    const float d = (float)__builtin_bit_cast(_Float16, scales[n * (K / kBlock) + (g * 16) / kBlock]);
+    const uint32_t w = codes[code_index(n, g, kw)];
+    const float d = (float)__builtin_bit_cast(_Float16, scales[scale_index(n, (g * 16) / kBlock, K / kBlock)]);
     float v[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -88,12 +91,22 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
         if (g < kw) {
             // Issue every load of this pass before any arithmetic, so the whole
             // pass costs one memory round trip.
+            // 16-byte loads of four rows' words and 8-byte loads of their scales
             uint32_t cw[RW];
             uint16_t db[RW];
+            const u4 *c4 = reinterpret_cast<const u4 *>(codes);
+            const uint2 *s4 = reinterpret_cast<const uint2 *>(scales);
 #pragma unroll
-            for (int r = 0; r < RW; ++r) cw[r] = codes[(int64_t)(n0 + r) * kw + g];
+            for (int i = 0; i < RW / 4; ++i) {
+                const u4 v = c4[(int64_t)((n0 >> 2) + i) * kw + g];
+                cw[4 * i] = v.x, cw[4 * i + 1] = v.y, cw[4 * i + 2] = v.z, cw[4 * i + 3] = v.w;
+            }
 #pragma unroll
-            for (int r = 0; r < RW; ++r) db[r] = scales[(int64_t)(n0 + r) * kb + (g >> 3)];
+            for (int i = 0; i < RW / 4; ++i) {
+                const uint2 v = s4[(int64_t)((n0 >> 2) + i) * kb + (g >> 3)];
+                db[4 * i] = (uint16_t)(v.x & 0xFFFFu), db[4 * i + 1] = (uint16_t)(v.x >> 16);
+                db[4 * i + 2] = (uint16_t)(v.y & 0xFFFFu), db[4 * i + 3] = (uint16_t)(v.y >> 16);
+            }
             f4 xr[MT][4];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
