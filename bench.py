@@ -43,6 +43,39 @@ def tq2_bytes(n, k):
     return n * (k // 128) * 34
 
 
+KERNEL_SOURCES = {  # files whose content defines each timed kernel
+    "gemv_f32_kernel": ["tq2_gemv.hip", "decode.h", "internal.h"],
+    "mfma_gemm_kernel": ["mfma_gemm.hip", "decode.h", "internal.h"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+CALIB_BYTES = 256 << 20   # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
+
+def source_sha(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "bit_weight_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, name):
+    """HBM bytes per launch from a committed counter summary, if the kernel source is unchanged."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha(kernel) or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -156,6 +189,74 @@ def bench_blr(torch, bw, steps, warmup):
     return t
 
 
+def calib_copy(torch, reps=5):
+    """Untimed device copies of known size, for scaling the HBM byte counters."""
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def summarize_stats(csv_path, command):
+    """Text summary of a rocprofv3 --stats kernel table (average duration per kernel)."""
+    import csv
+
+    rows = list(csv.DictReader(open(csv_path)))
+    print(f"# rocprofv3 kernel statistics")
+    print(f"# command: {command}")
+    print(f"# {'kernel':<90s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for r in rows:
+        print(f"  {r['Name'][:90]:<90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.3f} "
+              f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+
+
+def summarize_pmc(fetch_csv, write_csv, kernel, command_fetch, command_write):
+    """HBM traffic per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs, scaled by
+    what the same counters read for the plain copy of CALIB_BYTES."""
+    import csv
+
+    def values(path, name_part, counter):
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+
+    def mean_kib(path, name_part, counter):
+        vals = values(path, name_part, counter)
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    def copy_kib(path, counter):
+        # the runtime's device copy kernel; the calibration copies are its largest dispatches
+        vals = values(path, "copyBuffer", counter)
+        if not vals:
+            return None
+        top = [v for v in vals if v >= 0.9 * max(vals)]
+        return sum(top) / len(top)
+
+    f_k, nf = mean_kib(fetch_csv, kernel, "FETCH_SIZE")
+    w_k, nw = mean_kib(write_csv, kernel, "WRITE_SIZE")
+    f_c = copy_kib(fetch_csv, "FETCH_SIZE")
+    w_c = copy_kib(write_csv, "WRITE_SIZE")
+    kib = CALIB_BYTES / 1024
+    ff = kib / f_c if f_c else None
+    fw = kib / w_c if w_c else None
+    print("# HBM traffic per launch from rocprofv3 counters, scaled by a plain copy of known size")
+    print(f"# fetch command: {command_fetch}")
+    print(f"# write command: {command_write}")
+    print(f"kernel: {kernel}")
+    print(f"source_sha: {source_sha(kernel.split('<')[0])}")
+    print(f"dispatches_fetch: {nf}")
+    print(f"dispatches_write: {nw}")
+    print(f"fetch_kib_per_dispatch_raw: {f_k}")
+    print(f"write_kib_per_dispatch_raw: {w_k}")
+    print(f"copy_fetch_kib_raw: {f_c}")
+    print(f"copy_write_kib_raw: {w_c}")
+    print(f"copy_bytes: {CALIB_BYTES}")
+    print(f"fetch_scale: {ff}")
+    print(f"write_scale: {fw}")
+    if f_k is not None and w_k is not None and ff and fw:
+        print(f"hbm_bytes_per_launch: {(f_k * ff + w_k * fw) * 1024:.0f}")
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the decode workload."""
     import oracle
@@ -183,10 +284,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="decode,prefill,mlp,blr,cpu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
+                    help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "CMD_F", "CMD_W"),
+                    help="print HBM traffic per launch from two counter runs and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the ternary GEMM shards "
-              f"along N with no exchange, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the ternary GEMM "
+              f"shards along N with no exchange, so each GPU runs this same kernel on its N/G rows",
+              file=sys.stderr)
         sys.exit(2)
     only = set(args.only.split(","))
 
@@ -200,6 +312,8 @@ def main():
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
     K, W = args.steps, args.warmup
     out = {}
+    if "calib" in only:
+        calib_copy(torch)
     if "decode" in only:
         out["decode_f32"] = bench_decode(torch, bw, K, W, bw.TQ2_PATH_F32)
         out["decode_mfma"] = bench_decode(torch, bw, max(K // 4, 10), W, bw.TQ2_PATH_MFMA)
@@ -230,7 +344,8 @@ def main():
         line["value"] = round(d["gbs_step"], 2)
         line["ms_per_step"] = d["step_ms"]
         line["roofline"] = {"bound": "hbm", "achieved": round(d["gbs_step"], 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(d["gbs_step"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "unit": "GB/s", "frac": round(d["gbs_step"] / HBM_PEAK_GBS, 4),
+                            "traffic": read_traffic("gemv_f32_kernel", "gemv_f32_decode_M1_traffic.txt"),
                             "kernel": "gemv_f32_kernel", "kernel_us": round(d["step_ms"] * 1e3, 3)}
         line["eager_value"] = round(d["gbs_eager"], 2)
     if "prefill" in out:
