@@ -81,11 +81,16 @@ def log(msg):
 
 
 class Timer:
-    """W eager warmup steps, then K steps captured in one HIP graph and replayed
-    between two device synchronisations (HIP events on the launch stream bracket
-    the replay).  The graph removes host launch cost from the timed region; every
-    step is still one library call (one or more kernel launches).  The same K
-    steps issued eagerly from Python are timed too, as context."""
+    """W eager warmup steps, then K steps captured in one HIP graph; the graph is
+    replayed once untimed and then REPS times, each replay bracketed by HIP events
+    on the launch stream and by device synchronisations.  The per-step time is
+    the median replay / K (the minimum is reported too).  The graph removes host
+    launch cost from the timed region; every step is still one library call (one
+    or more kernel launches).  Warmup, capture and replays use one stream, so
+    per-stream library state (the split-K scratch) exists before the capture.
+    The same K steps issued eagerly from Python are timed too, as context."""
+
+    REPS = 11
 
     def __init__(self, torch):
         self.torch = torch
@@ -97,33 +102,37 @@ class Timer:
         with torch.cuda.stream(side):
             for i in range(warmup):
                 fn(i)
-        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        with torch.cuda.graph(graph, stream=side):
             for i in range(steps):
                 fn(i)
-        graph.replay()  # untimed first replay
+        with torch.cuda.stream(side):
+            graph.replay()  # untimed first replay
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        regions = []
         t0 = time.perf_counter()
-        start.record()
-        graph.replay()
-        end.record()
-        torch.cuda.synchronize()
+        for _ in range(self.REPS):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                start.record(side)
+                graph.replay()
+                end.record(side)
+            torch.cuda.synchronize()
+            regions.append(start.elapsed_time(end))
         wall = time.perf_counter() - t0
-        region_ms = start.elapsed_time(end)
         del graph
         # the same steps issued eagerly (host launch cost included), for context
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            fn(i)
-        e1.record()
+        with torch.cuda.stream(side):
+            e0.record(side)
+            for i in range(steps):
+                fn(i)
+            e1.record(side)
         torch.cuda.synchronize()
-        return dict(region_ms=region_ms, step_ms=region_ms / steps, host_wall_s=wall,
+        med = float(np.median(regions))
+        return dict(region_ms=med, region_ms_all=[round(r, 4) for r in regions], step_ms=med / steps,
+                    step_ms_min=min(regions) / steps, reps=self.REPS, host_wall_s=wall,
                     eager_step_ms=e0.elapsed_time(e1) / steps)
 
 
@@ -343,6 +352,9 @@ def main():
         d = out["decode_f32"]
         line["value"] = round(d["gbs_step"], 2)
         line["ms_per_step"] = d["step_ms"]
+        line["ms_per_step_min"] = d["step_ms_min"]
+        line["timing"] = (f"median (and min) over {d['reps']} replays of one HIP graph holding the K steps, "
+                          f"HIP events on the launch stream")
         line["roofline"] = {"bound": "hbm", "achieved": round(d["gbs_step"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["gbs_step"] / HBM_PEAK_GBS, 4),
                             "traffic": read_traffic("gemv_f32_kernel", "gemv_f32_decode_M1_traffic.txt"),
@@ -352,6 +364,7 @@ def main():
         p = out["prefill"]
         line["prefill"] = {"workload": "tq2_gemm M=2048, N=4096, K=4096 (MFMA f16 path, x staged to f16)",
                            "tflops": round(p["tflops_step"], 2), "ms_per_call": p["step_ms"],
+                           "ms_per_call_min": p["step_ms_min"],
                            "roofline": {"bound": "mfma", "achieved": round(p["tflops_step"], 2),
                                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(p["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4),
@@ -359,16 +372,19 @@ def main():
                                         "kernel_us": round(p["step_ms"] * 1e3, 3)}}
     if "decode_mfma" in out:
         line["decode_mfma_path"] = {"gbs": round(out["decode_mfma"]["gbs_step"], 2),
-                                    "us_per_call": round(out["decode_mfma"]["step_ms"] * 1e3, 3)}
+                                    "us_per_call": round(out["decode_mfma"]["step_ms"] * 1e3, 3),
+                                    "us_per_call_min": round(out["decode_mfma"]["step_ms_min"] * 1e3, 3)}
     for key in [k for k in out if k.startswith("mlp_")]:
         v = out[key]
         line[key] = {"gbs": round(v["gbs_step"], 2), "tflops": round(v["tflops_step"], 3),
                      "us_per_call": round(v["step_ms"] * 1e3, 3),
+                     "us_per_call_min": round(v["step_ms_min"] * 1e3, 3),
                      "hbm_frac": round(v["gbs_step"] / HBM_PEAK_GBS, 4)}
     if "blr" in out:
         b = out["blr"]
         line["blr"] = {"workload": "blr_forward M=512, d_in=d_out=4096, r=1024 (4 launches per call)",
                        "tflops": round(b["tflops_step"], 2), "ms_per_call": b["step_ms"],
+                       "ms_per_call_min": b["step_ms_min"],
                        "mfma_frac": round(b["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4)}
     if "cpu" in only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -40,7 +40,16 @@ struct DevWeight {
 // Each launcher validates nothing (the C-ABI layer has) and returns the HIP status.
 hipError_t launch_dequant(const DevWeight &w, float *out, hipStream_t s);
 hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
+
+// MFMA path (any M; small M uses 64-column tiles with the K range split over
+// the waves of each workgroup).
 hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
+
+// Skinny MFMA kernel for M <= kSkinnyMaxM whose x (as f16) fits in LDS.
+constexpr int64_t kSkinnyMaxM = 16;
+constexpr size_t kSkinnyMaxLds = 128 * 1024;
+bool skinny_fits(const DevWeight &w, int64_t M);
+hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s);
 
 // Binary low-rank forward.  Workspace carve-up is computed by blr_plan.
 struct BlrPlan {

@@ -231,8 +231,13 @@ int tq2_gemm_path(const tq2_weight *w, const float *x, float *y, int64_t M, int6
     if (path == TQ2_PATH_AUTO) path = tq2_select_path(M);
     if (path == TQ2_PATH_MFMA && !w->dev.mfma_ok) path = TQ2_PATH_F32;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = (path == TQ2_PATH_F32) ? tq2::launch_gemv_f32(w->dev, x, y, M, s)
-                                          : tq2::launch_gemm_mfma(w->dev, x, y, M, s);
+    hipError_t e;
+    if (path == TQ2_PATH_F32)
+        e = tq2::launch_gemv_f32(w->dev, x, y, M, s);
+    else if (tq2::skinny_fits(w->dev, M))
+        e = tq2::launch_skinny(w->dev, x, y, M, dev, s);
+    else
+        e = tq2::launch_gemm_mfma(w->dev, x, y, M, s);
     return from_hip(e);
 }
 

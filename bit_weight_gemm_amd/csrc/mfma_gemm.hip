@@ -49,29 +49,62 @@ struct GemmArgs {
     int a_vec;               // A rows and column factors allow 16-byte loads (K % 4 == 0, aligned)
 };
 
-// 16-byte chunk `kc` (8 halves) of tile row `row`, XOR-swizzled across the row.
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * BK + ((kc ^ (row & 7)) << 3); }
+// LDS has 64 four-byte banks on gfx950: a 16-byte read serves 16 lanes per
+// cycle, a 4-byte access 64 lanes.  Both swizzles below keep every such group
+// on distinct banks (and also do so for a 32-bank LDS).
+//
+// A tile: 16-byte chunk `kc` (8 halves) of tile row `row`, NCH chunks per row.
+// A fragment read has 16 lanes on 16 consecutive rows at one kc.  With 8 chunks
+// (128 bytes) per row, rows r and r+1 are 32 banks apart, so the chunk
+// permutation must differ between rows r and r+8 as well as within each group
+// of 8 rows; with 16 or more chunks per row every row starts on bank 0 and the
+// permutation must differ over 16 rows.
+template <int NCH>
+__device__ __forceinline__ int lds_off(int row, int kc) {
+    const int g = NCH == 8 ? (row & 7) ^ ((row >> 3) & 1) : (row & 15);
+    return row * (NCH * 8) + ((kc ^ g) << 3);
+}
+// B tile: slot of row R's 16-byte unit (its four code words of a 64-wide k
+// slice).  The transposing store writes word g of rows 4q+r from lane 4q+g, the
+// fragment read takes the units of 16 consecutive rows; this permutation within
+// each group of 16 rows spreads both over all banks.
+__device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15); }
 
-// AMODE: how A tiles are read.  kAExact: M and K tile exactly or rows past M are
-// clamped (ternary GEMM, K a multiple of 64).  kAVec: 16-byte loads with clamped
-// addresses and zeroing past M and K (needs K % 4 == 0 and 16-byte aligned rows).
-// kAScalar: element-wise guarded loads (any K).
-enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2 };
+// AMODE: how A tiles are read.  kAExact: K is a multiple of the step and rows
+// past M read row M-1 (ternary GEMM).  kAVec: 16-byte loads with clamped
+// addresses and zeroing past K (needs K % 4 == 0 and 16-byte aligned rows).
+// kAScalar: element-wise guarded loads (any K).  kABuf: as kAExact, but through
+// a buffer resource spanning the M rows, so loads of rows past M return zero
+// without a memory request (small M, M*lda*4 < 2^31).  Rows past M only reach
+// output rows that are never stored.
+enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2, kABuf = 3 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
-    constexpr int T = WM * WN * 64;
+// Workgroup: WK groups of WM x WN waves.  Each step covers SK = 64*WK of K; wave
+// group wk takes the 64-wide slice wk of every step, and the groups' partial
+// tiles are added through LDS at the end (wk = 0, 1, ... in order).
+template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool COLF, bool SCALED,
+          int EPI>
+__global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) {
+    constexpr int NW = WM * WN;  // waves per k group
+    constexpr int T = NW * WK * 64;
+    constexpr int SK = BK * WK;  // k per step
+    constexpr int NCH = SK / 8;
+    constexpr int NBLK = (SK + kBlock - 1) / kBlock;  // scale blocks per step
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MB = WTM / 32, NB = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-
     static_assert(STAGES >= 2, "at least two pipeline stages");
-    __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][BN * 4];  // 4 code words (64 k) per B row
-    __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][BN];      // B row scale for the step
+    static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
+    static_assert(AMODE != kABuf || !COLF, "buffer-loaded A has no column factors");
+    static_assert(WK == 1 || (WK - 1) * BM * BN * 4 <= STAGES * BM * SK * 2, "k-group sums must fit the A tiles");
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * SK];
+    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][WK][BN * 4];  // 4 code words per row and slice
+    __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][NBLK][BN];     // B row scales of the step
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wk = wave / NW, wr = wave % NW;
+    const int wm = wr / WN, wn = wr % WN;
     const int lrow = lane & 31, hk = lane >> 5;
     const uint32_t magic = f16_magic();
 
@@ -90,34 +123,49 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f16x{};
 
-    // Two register stages of prefetch: the loads for step k+2 are issued while
-    // step k computes, so each global load has two compute phases to land.  Every
-    // loaded value (A as f16, B code words and scales) goes through LDS, so a
-    // stage's registers are free again right after the LDS store at the top of
-    // its step.
+    // Register stages of prefetch (see the pipeline below): STAGES for A, BDEPTH
+    // for B.  Every loaded value (A as f16, B code words and scales) goes through
+    // LDS, so a stage's registers are free again right after its LDS store.  B
+    // (the weight stream) may run further ahead than A (which other workgroups
+    // share through L2), to keep enough HBM reads in flight when the tiles are
+    // few.
     // B arrives in 16-byte units holding one 16-element group of four rows; a
-    // step needs BN units (BN/4 row quads x 4 groups), BPT per thread.
-    constexpr int BPT = (BN + T - 1) / T;
+    // step needs BN*WK units (BN/4 row quads x 4*WK groups), BPT per thread.
+    // When there are fewer units than threads, thread t takes unit t % BITEMS
+    // (duplicates load and store the same values), keeping the loop free of
+    // branches; the 8-byte scale units (one row quad, one block) likewise.
+    constexpr int BITEMS = BN * WK;
+    constexpr int BPT = (BITEMS + T - 1) / T;
+    static_assert(BITEMS % T == 0 || BITEMS < T, "B units: a multiple of the threads, or fewer");
+    constexpr int DITEMS = (BN / 4) * NBLK;
+    static_assert(DITEMS <= T && T % DITEMS == 0, "scale units must tile the threads");
     // A is moved in 16-byte pieces (4 floats): piece q of tile row r covers
-    // k = 4q..4q+3; consecutive lanes take consecutive pieces of a row, so each
-    // wave-wide load reads whole 256-byte row segments.
-    constexpr int PIECES = BM * (BK / 4);
+    // k = 4q..4q+3 of the step; consecutive lanes take consecutive pieces of a
+    // row, so each wave-wide load reads whole row segments.
+    constexpr int QPR = SK / 4;  // pieces per row
+    constexpr int PIECES = BM * QPR;
     constexpr int PPT = PIECES / T;
     static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
     f4 areg[STAGES][PPT];
     f4 creg[STAGES][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
-    u4 breg[STAGES][BPT];
-    uint2 dreg[STAGES];  // scales of one row quad (threads tid < BN/4)
+    u4 breg[BDEPTH][BPT];
+    uint2 dreg[BDEPTH];  // scales of one row quad and block
 
+    // (only kABuf reads through it; unused otherwise)
+    const int64_t abytes = (int64_t)p.M * p.lda * 4;
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(p.A), (short)0, abytes < 0x7fffffff ? (int)abytes : 0x7fffffff, 0x00020000);
     auto load_a = [&](int st, int k0) {
 #pragma unroll
         for (int c = 0; c < PPT; ++c) {
             const int piece = tid + c * T;
-            const int row = piece >> 4, q = piece & 15;
+            const int row = piece / QPR, q = piece % QPR;
             const int gm = m0 + row, gk = k0 + q * 4;
-            // rows past M read row M-1 (valid memory); store() zeroes them
+            // rows past M read row M-1 (valid memory); their output rows are not stored
             const int gmc = gm < p.M ? gm : p.M - 1;
-            if constexpr (AMODE == kAExact) {
+            if constexpr (AMODE == kABuf) {
+                areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (gm * (int)p.lda + gk) * 4, 0, 0));
+            } else if constexpr (AMODE == kAExact) {
                 areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
                 if constexpr (COLF) creg[st][c] = *reinterpret_cast<const f4 *>(p.colf + gk);
             } else if constexpr (AMODE == kAVec) {
@@ -147,60 +195,57 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
         const u4 *c4 = reinterpret_cast<const u4 *>(p.codes);
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int item = tid + i * T;
-            if (BN % T == 0 || item < BN) {
-                const int64_t quad = (n0 >> 2) + (item >> 2);
-                breg[st][i] = c4[quad * p.kw + (k0 >> 4) + (item & 3)];
-            }
+            const int item = (tid + i * T) % BITEMS;
+            const int64_t quad = (n0 >> 2) + item / (4 * WK);
+            breg[st][i] = c4[quad * p.kw + (k0 >> 4) + item % (4 * WK)];
         }
-        if constexpr (SCALED) {
-            if (tid < BN / 4) {
-                const uint2 *s4 = reinterpret_cast<const uint2 *>(p.scales);
-                dreg[st] = s4[((n0 >> 2) + tid) * p.kbw + k0 / kBlock];
-            }
+        // whole waves past DITEMS skip the scales (a wave-uniform branch)
+        if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
+            const uint2 *s4 = reinterpret_cast<const uint2 *>(p.scales);
+            const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
+            dreg[st] = s4[((n0 >> 2) + quad) * p.kbw + k0 / kBlock + blk];
         }
     };
-    auto store = [&](int st, int k0) {
+    // store(st, sa, sb): A register stage sa and B register stage sb into LDS buffer st
+    auto store = [&](int st, int sa, int sb) {
 #pragma unroll
         for (int c = 0; c < PPT; ++c) {
             const int piece = tid + c * T;
-            const int row = piece >> 4, q = piece & 15;
+            const int row = piece / QPR, q = piece % QPR;
             typedef _Float16 h4 __attribute__((ext_vector_type(4)));
             h4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float a = areg[st][c][e];
-                if constexpr (COLF) a = a * creg[st][c][e];  // factors past K are 0
+                float a = areg[sa][c][e];
+                if constexpr (COLF) a = a * creg[sa][c][e];  // factors past K are 0
                 v[e] = (_Float16)a;
             }
-            if (AMODE != kAScalar && m0 + row >= p.M) v = h4{};  // clamped rows past M contribute zero
-            *reinterpret_cast<h4 *>(&As[st][lds_off(row, q >> 1) + ((q & 1) << 2)]) = v;
+            *reinterpret_cast<h4 *>(&As[st][lds_off<NCH>(row, q >> 1) + ((q & 1) << 2)]) = v;
         }
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int item = tid + i * T;
-            if (BN % T == 0 || item < BN) {
-                const int r0 = (item >> 2) * 4, g = item & 3;
+            const int item = (tid + i * T) % BITEMS;
+            const int r0 = (item / (4 * WK)) * 4, g = item % (4 * WK);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Bs[st][(r0 + r) * 4 + g] = breg[st][i][r];
-            }
+            for (int r = 0; r < 4; ++r) Bs[st][g >> 2][b_slot(r0 + r) * 4 + (g & 3)] = breg[sb][i][r];
         }
-        if constexpr (SCALED) {
-            if (tid < BN / 4) *reinterpret_cast<uint2 *>(&Ds[st][4 * tid]) = dreg[st];
+        if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
+            const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
+            *reinterpret_cast<uint2 *>(&Ds[st][blk][4 * quad]) = dreg[sb];
         }
     };
 
-    // compute(st, hook): the MFMAs of the step in LDS buffer st; hook() runs after
-    // the first 16-wide sub-step, so the staging of the next step overlaps the
-    // remaining MFMAs of this one.
+    // compute(st, hook): the MFMAs of this wave's 64-wide slice of the step in
+    // LDS buffer st; hook() runs after the first 16-wide sub-step, so the staging
+    // of the next step overlaps the remaining MFMAs of this one.
     auto compute = [&](int st, auto &&hook) {
         u4 bw[NB];
         _Float16 dv[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int row = wn * WTN + nb * 32 + lrow;
-            bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][row * 4]);
-            dv[nb] = SCALED ? Ds[st][row] : (_Float16)1.0f;
+            bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][wk][b_slot(row) * 4]);
+            dv[nb] = SCALED ? Ds[st][(wk * BK) / kBlock][row] : (_Float16)1.0f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -208,7 +253,7 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = wm * WTM + mb * 32 + lrow;
-                a[mb] = *reinterpret_cast<const h8 *>(&As[st][lds_off(row, 2 * j + hk)]);
+                a[mb] = *reinterpret_cast<const h8 *>(&As[st][lds_off<NCH>(row, wk * 8 + 2 * j + hk)]);
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -226,39 +271,63 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
 
     // Pipeline: register stages hold steps loaded from memory but not yet in LDS;
     // LDS buffer t % STAGES holds step t.  While step t computes, step t+1 moves
-    // from registers to LDS and its register stage is refilled with step
-    // t+1+STAGES (loads issued STAGES steps before they are stored).  One
-    // barrier per step makes step t+1's tile visible; buffer (t+1) % STAGES was
-    // last read by step t+1-STAGES <= t-1, which every wave finished before the
-    // barrier that ended step t-1.  Kloop is a multiple of STAGES*BK, so the loop
-    // is branch-free; loads and stores past the end use clamped addresses and
-    // are never read.
-    const int nsteps = p.Kloop / BK;
-    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * BK; };
+    // from registers to LDS, and its register stages are refilled: A's with step
+    // t+1+STAGES, B's with step t+1+BDEPTH (loads issued STAGES, or BDEPTH,
+    // steps before they are stored).  One barrier per step makes step t+1's tile
+    // visible; buffer (t+1) % STAGES was last read by step t+1-STAGES <= t-1,
+    // which every wave finished before the barrier that ended step t-1.  The
+    // step count is a multiple of BDEPTH, so the loop is branch-free; loads and
+    // stores past the end use clamped addresses and are never read.
+    const int nsteps = p.Kloop / SK;
+    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * SK; };
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st) {
-        load_a(st, st * BK);
-        load_b(st, st * BK);
+    for (int st = 0; st < BDEPTH; ++st) {
+        if (st < STAGES) load_a(st, st * SK);
+        load_b(st, clampk(st));
         __builtin_amdgcn_sched_barrier(0);
     }
-    store(0, 0);
+    store(0, 0, 0);
     load_a(0, clampk(STAGES));
-    load_b(0, clampk(STAGES));
+    load_b(0, clampk(BDEPTH));
     __syncthreads();
-    for (int t0 = 0; t0 < nsteps; t0 += STAGES) {
+    for (int t0 = 0; t0 < nsteps; t0 += BDEPTH) {
 #pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
+        for (int s = 0; s < BDEPTH; ++s) {
             const int t = t0 + s;
-            constexpr int dummy = 0;
-            (void)dummy;
-            const int nx = (s + 1) % STAGES;  // register stage and LDS buffer of step t+1
-            compute(s, [&] {
-                store(nx, clampk(t + 1));
-                load_a(nx, clampk(t + 1 + STAGES));
-                load_b(nx, clampk(t + 1 + STAGES));
+            const int nbuf = (s + 1) % STAGES;  // LDS buffer and A register stage of step t+1
+            const int nsb = (s + 1) % BDEPTH;  // B register stage of step t+1
+            compute(s % STAGES, [&] {
+                store(nbuf, nbuf, nsb);
+                load_a(nbuf, clampk(t + 1 + STAGES));
+                load_b(nsb, clampk(t + 1 + BDEPTH));
             });
             __syncthreads();
         }
+    }
+
+    if constexpr (WK > 1) {
+        // k groups 1..WK-1 leave their partial tiles in LDS (over the A tiles,
+        // which the loop no longer reads); group 0 adds them in group order.
+        float *red = reinterpret_cast<float *>(&As[0][0]);
+        auto at = [&](int g, int mb, int nb, int r) { return (((g * NW + wr) * MB + mb) * NB + nb) * 1024 + r * 64 + lane; };
+        if (wk > 0) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[at(wk - 1, mb, nb, r)] = acc[mb][nb][r];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int g = 1; g < WK; ++g)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mb][nb][r] += red[at(g - 1, mb, nb, r)];
     }
 
     // ---- epilogue: lane holds column lrow, rows 8*(r/4) + 4*hk + r%4 of each block
@@ -280,18 +349,20 @@ __global__ __launch_bounds__(WM *WN * 64) void mfma_gemm_kernel(GemmArgs p) {
         }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI>
-static hipError_t run_gemm(GemmArgs p, int64_t npad, hipStream_t s) {
-    p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= npad, so B rows stay in bounds
-    (void)npad;
+template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI,
+          int BDEPTH = STAGES>
+static hipError_t run_gemm(GemmArgs p, hipStream_t s) {
+    p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
-    mfma_gemm_kernel<BM, BN, WM, WN, STAGES, AMODE, COLF, SCALED, EPI>
-        <<<dim3((unsigned)tiles), dim3(WM * WN * 64), 0, s>>>(p);
+    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, COLF, SCALED, EPI>
+        <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ ternary GEMM, large M
+
+static int mfma_stages(int64_t K) { return (K / BK) % 4 == 0 ? 4 : 2; }
 
 hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s) {
     GemmArgs p{};
@@ -311,12 +382,25 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     p.Kloop = (int)w.K;
     p.a_vec = 1;
     // K is a multiple of 128 (two steps); four stages when the step count allows
-    const bool four = (w.K / BK) % 4 == 0;
+    const bool four = mfma_stages(w.K) == 4;
+    // Small M: 64-column tiles whose four waves of each column half split the
+    // step's K four ways (two ways when K has too few blocks), so N/64
+    // workgroups of eight waves stream the weight.  Up to 32 rows, A comes
+    // through a buffer resource, so the rows past M cost no memory traffic.
+    const int64_t kb = w.K / kBlock;
+    if (M <= 32 && M * w.K * 4 < ((int64_t)1 << 31)) {
+        if (kb % 8 == 0) return run_gemm<32, 64, 1, 2, 4, 4, kABuf, false, true, kEpiStore>(p, s);
+        if (kb % 4 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, false, true, kEpiStore>(p, s);
+        if (kb % 2 == 0) return run_gemm<32, 64, 1, 2, 2, 2, kABuf, false, true, kEpiStore>(p, s);
+    } else if (M <= 64) {
+        if (kb % 4 == 0) return run_gemm<64, 64, 1, 2, 2, 4, kAExact, false, true, kEpiStore>(p, s);
+        if (kb % 2 == 0) return run_gemm<64, 64, 1, 2, 2, 2, kAExact, false, true, kEpiStore>(p, s);
+    }
     if (M <= 64)
-        return four ? run_gemm<32, 256, 1, 4, 4, kAExact, false, true, kEpiStore>(p, w.Npad, s)
-                    : run_gemm<32, 256, 1, 4, 2, kAExact, false, true, kEpiStore>(p, w.Npad, s);
-    return four ? run_gemm<128, 256, 1, 4, 4, kAExact, false, true, kEpiStore>(p, w.Npad, s)
-                : run_gemm<128, 256, 1, 4, 2, kAExact, false, true, kEpiStore>(p, w.Npad, s);
+        return four ? run_gemm<32, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
+                    : run_gemm<32, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
+    return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
+                : run_gemm<128, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
 }
 
 // ------------------------------------------------------------------ binary low-rank forward
@@ -416,8 +500,8 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p1.M = (int)pl.M, p1.N = (int)pl.r, p1.K = (int)pl.d_in, p1.Kloop = (int)pl.kpad1;
     p1.a_vec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
                ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
-    hipError_t e = p1.a_vec ? run_gemm<64, kBlrBN, 2, 2, 4, kAVec, true, false, kEpiStore>(p1, pl.npad1, s)
-                            : run_gemm<64, kBlrBN, 2, 2, 4, kAScalar, true, false, kEpiStore>(p1, pl.npad1, s);
+    hipError_t e = p1.a_vec ? run_gemm<64, kBlrBN, 2, 2, 1, 4, kAVec, true, false, kEpiStore>(p1, s)
+                            : run_gemm<64, kBlrBN, 2, 2, 1, 4, kAScalar, true, false, kEpiStore>(p1, s);
     if (e != hipSuccess) return e;
     // GEMM2: y[M][d_out] = h . (f16(a.l) . S_U^T)
     GemmArgs p2{};
@@ -427,8 +511,8 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.r, p2.Kloop = (int)pl.kpad2;
     // a is the 256-byte aligned workspace and r % 32 == 0; l decides
     p2.a_vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
-    return p2.a_vec ? run_gemm<64, kBlrBN, 2, 2, 4, kAVec, true, false, kEpiRowScale>(p2, pl.npad2, s)
-                    : run_gemm<64, kBlrBN, 2, 2, 4, kAScalar, true, false, kEpiRowScale>(p2, pl.npad2, s);
+    return p2.a_vec ? run_gemm<64, kBlrBN, 2, 2, 1, 4, kAVec, true, false, kEpiRowScale>(p2, s)
+                    : run_gemm<64, kBlrBN, 2, 2, 1, 4, kAScalar, true, false, kEpiRowScale>(p2, s);
 }
 
 }  // namespace tq2

@@ -1,0 +1,244 @@
+// Skinny MFMA product for few activation rows: y[m][n] = sum_k f16(x[m][k]) *
+// (code-1)*d, the ternary GEMM of "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs"
+// on the f16 MFMA path (same operands and bound as the tiled kernel).
+//
+// For M <= 16 the whole of x fits in LDS as f16, so a workgroup stages it once
+// and its waves then run without barriers: each wave streams the code words of
+// the workgroup's 32 output columns over its own share of K (a half, quarter or
+// eighth) straight from HBM into registers, several steps ahead, decodes them and issues
+// v_mfma_f32_32x32x16_f16 with A fragments read from LDS.  At the end the waves'
+// partial tiles are added through LDS in wave order, so the result does not
+// depend on timing.  Workgroups are N/32, so every CU takes part even when N is
+// a few thousand.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "decode.h"
+#include "internal.h"
+
+namespace tq2 {
+
+namespace {
+
+struct SkinnyArgs {
+    const float *x;          // [M][K] f32
+    const uint32_t *codes;   // device layout (code_index)
+    const uint16_t *scales;  // device layout (scale_index)
+    float *y;                // [M][N]
+    int M, N, K;
+    int kw, kb;              // K/16, K/128
+};
+
+// x in LDS: row r at r*(K+8) halves.  K is a multiple of 128, so each row
+// starts 16 bytes further round the 64 banks than the one before, and the 16
+// rows read by one A-fragment access land on 16 different bank groups.
+__device__ __forceinline__ int xs_row(int r, int K) { return r * (K + 8); }
+
+// NBW: 32-column blocks per wave (and per workgroup); WK: waves, each owning
+// K/WK of the contraction; D: steps of 64 k whose code words are in flight;
+// U: pieces of x (4 values) each thread stages, with WK*64*U >= M*K/4.
+template <int NBW, int WK, int D, int U>
+__global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lrow = lane & 31, hk = lane >> 5;
+    const int n0 = blockIdx.x * (32 * NBW);
+    const uint32_t magic = f16_magic();
+
+    // ---- this wave's K range and its code-word stream
+    const int kw_wave = p.K / WK;      // k per wave, a multiple of 64
+    const int nsteps = kw_wave / 64;   // a multiple of D
+    const int kbeg = wave * kw_wave;
+    int col[NBW];
+    uint32_t cbase[NBW], sbase[NBW];  // word offsets of (col, group kbeg/16) and (col, block kbeg/128)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+        col[nb] = n0 + 32 * nb + lrow;  // < Npad: padded rows are code 1
+        cbase[nb] = (uint32_t)code_index(col[nb], kbeg >> 4, p.kw);
+        sbase[nb] = (uint32_t)scale_index(col[nb], kbeg / kBlock, p.kb);
+    }
+    uint32_t bw[D][NBW][4];
+    uint16_t dv[D][NBW];
+    // step t: groups kbeg/16 + 4t .. +3 (16 words apart per step, 4 per group),
+    // block kbeg/128 + t/2 (4 scales apart per block)
+    auto load = [&](int slot, int t) {
+        const uint32_t tc = (uint32_t)(t < nsteps ? t : nsteps - 1);  // clamped past the end
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const uint32_t *cw = p.codes + cbase[nb] + 16 * tc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bw[slot][nb][i] = cw[4 * i];
+            dv[slot][nb] = p.scales[sbase[nb] + 4 * (tc >> 1)];
+        }
+    };
+    // ---- stage x once: f32 -> f16 (round to nearest even), 4 values per piece;
+    // a thread stages U pieces of [M][K/4] (row-major), T apart, and T*U covers
+    // all of x.  The loads go out before the weight stream starts and the LDS
+    // stores wait only for them (the memory counter retires in issue order), so
+    // x comes from L2 while the first code words are still on their way from
+    // HBM.  Slots past the end re-read the thread's first piece and store
+    // nothing, which keeps the loads free of branches.
+    const int per_row = p.K / 4;
+    const int total = p.M * per_row;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    constexpr int T = WK * 64;
+    const int adv_r = T / per_row, adv_q = T % per_row;  // (row, q) advance per T pieces
+    f4 xv[U];
+    // Each workgroup walks x from its own starting piece (wrapping at the end),
+    // so the workgroups on one XCD do not all ask the same L2 channel for the
+    // same line at once.  Piece u of this thread is (start + tid + u*T) mod
+    // M*K/4, tracked as (row, q) and advanced without divisions.
+    const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
+    const int s0 = (tid + start) % total;
+    const int r0 = s0 / per_row, q0 = s0 % per_row;
+    const int adv_rm = adv_r % p.M;
+    auto next = [&](int &r, int &q) {
+        q += adv_q;
+        r += adv_rm;
+        if (q >= per_row) {
+            q -= per_row;
+            ++r;
+        }
+        if (r >= p.M) r -= p.M;
+    };
+    {
+        int r = r0, q = q0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = u * T + tid < total;
+            xv[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + 4 * (live ? q : q0));
+            next(r, q);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code-word loads
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        int r = r0, q = q0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u * T + tid < total) {
+                const h4 h = {(_Float16)xv[u][0], (_Float16)xv[u][1], (_Float16)xv[u][2], (_Float16)xv[u][3]};
+                *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + 4 * q]) = h;
+            }
+            next(r, q);
+        }
+    }
+
+    f16x acc[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[nb] = f16x{};
+    const int arow = lrow < p.M ? lrow : p.M - 1;  // rows past M repeat row M-1; never stored
+
+    // x is in LDS once every wave's stores are done; a plain barrier, so the
+    // code words in flight are not waited for here
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int t0 = 0; t0 < nsteps; t0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const _Float16 *xa = xs + xs_row(arow, p.K) + kbeg + (t0 + s) * 64 + 8 * hk;
+            h8 a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const h8 *>(xa + 16 * j);
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const _Float16 d = __builtin_bit_cast(_Float16, dv[s][nb]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const h8 b = half_group_m1(bw[s][nb][j], hk, magic) * d;
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b, acc[nb], 0, 0, 0);
+                }
+            }
+            load(s, t0 + s + D);
+        }
+    }
+
+    // ---- add the waves' partial tiles in wave order (LDS reused after the barrier)
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(xs);
+    auto at = [&](int w, int nb, int r) { return ((w * NBW + nb) * 16 + r) * 64 + lane; };
+    if (wave > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[at(wave - 1, nb, r)] = acc[nb][r];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll 1
+    for (int w = 1; w < WK; ++w)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][r] += red[at(w - 1, nb, r)];
+    // lane holds column lrow of each block, rows 8*(r/4) + 4*hk + r%4
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+        const int gn = col[nb];
+        if (gn >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int gm = 8 * (r >> 2) + 4 * hk + (r & 3);
+            if (gm < p.M) p.y[(int64_t)gm * p.N + gn] = acc[nb][r];
+        }
+    }
+}
+
+template <int NBW, int WK, int D, int U>
+hipError_t run_skinny(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+    // raise the kernel's dynamic LDS limit once per device (bit dev of the mask)
+    static std::atomic<uint64_t> attr_set{0};
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!bit || !(attr_set.load() & bit)) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<NBW, WK, D, U>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(bit);
+    }
+    const unsigned blocks = (unsigned)((a.N + 32 * NBW - 1) / (32 * NBW));
+    skinny_kernel<NBW, WK, D, U><<<dim3(blocks), dim3(WK * 64), lds, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool skinny_fits(const DevWeight &w, int64_t M) {
+    // eight waves of 64 k-wide steps: K % 512 == 0; x staged in one round of at
+    // most 16 pieces per thread: M*K/4 <= 512*16
+    return M >= 1 && M <= kSkinnyMaxM && w.K % 512 == 0 && M * w.K <= 4 * 512 * 16;
+}
+
+hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s) {
+    SkinnyArgs a{};
+    a.x = x;
+    a.codes = w.codes;
+    a.scales = w.scales;
+    a.y = y;
+    a.M = (int)M;
+    a.N = (int)w.N;
+    a.K = (int)w.K;
+    a.kw = (int)(w.K / 16);
+    a.kb = (int)(w.K / kBlock);
+    // Eight waves; wave w owns K/8, i.e. K/512 steps, in a multiple of the
+    // prefetch depth D.  LDS: x as f16 (padded rows), later the waves' sums.
+    const size_t xb = (size_t)M * (w.K + 8) * 2, rb = (size_t)7 * 16 * 64 * 4;
+    const size_t lds = xb > rb ? xb : rb;
+    const int64_t steps = w.K / 512;
+    const bool small = M * w.K <= 4 * 512 * 2;  // two pieces per thread suffice
+    // one workgroup per CU: 64 columns per workgroup once 32-column ones would
+    // outnumber the CUs
+    if ((w.N + 31) / 32 > 256) {
+        const size_t lds2 = xb > 2 * rb ? xb : 2 * rb;
+        if (steps % 4 == 0) return small ? run_skinny<2, 8, 4, 2>(a, lds2, dev, s) : run_skinny<2, 8, 4, 16>(a, lds2, dev, s);
+        if (steps % 2 == 0) return small ? run_skinny<2, 8, 2, 2>(a, lds2, dev, s) : run_skinny<2, 8, 2, 16>(a, lds2, dev, s);
+        return small ? run_skinny<2, 8, 1, 2>(a, lds2, dev, s) : run_skinny<2, 8, 1, 16>(a, lds2, dev, s);
+    }
+    if (steps % 8 == 0) return small ? run_skinny<1, 8, 8, 2>(a, lds, dev, s) : run_skinny<1, 8, 8, 16>(a, lds, dev, s);
+    if (steps % 4 == 0) return small ? run_skinny<1, 8, 4, 2>(a, lds, dev, s) : run_skinny<1, 8, 4, 16>(a, lds, dev, s);
+    if (steps % 2 == 0) return small ? run_skinny<1, 8, 2, 2>(a, lds, dev, s) : run_skinny<1, 8, 2, 16>(a, lds, dev, s);
+    return small ? run_skinny<1, 8, 1, 2>(a, lds, dev, s) : run_skinny<1, 8, 1, 16>(a, lds, dev, s);
+}
+
+}  // namespace tq2

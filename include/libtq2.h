@@ -74,7 +74,8 @@ int tq2_weight_info(const tq2_weight *w, int64_t *N, int64_t *K, size_t *device_
  * x: device f32 [M][K] row-major, 16-byte aligned; y: device f32 [M][N] row-major,
  * 16-byte aligned, overwritten, must not overlap x.  N and K must equal the
  * handle's.  M == 0 is a successful no-op.  Asynchronous on `stream`.
- * The path follows tq2_select_path(M); both paths are deterministic (no atomics). */
+ * The path follows tq2_select_path(M).  Results are deterministic: repeated calls
+ * with the same inputs give the same bits.  No device memory is allocated. */
 int tq2_gemm(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* tq2_gemm on an explicitly chosen path (TQ2_PATH_AUTO, _F32 or _MFMA).

@@ -1,0 +1,67 @@
+"""GPU parity of the MFMA path's small-M tiles with the oracle.
+
+For M <= 64 the MFMA path uses 64-column tiles whose waves split each step's K
+range (four ways when the block count K/128 is a multiple of 4, two ways when
+it is even) and add their partial tiles in a fixed order at the end; an odd
+block count takes the 256-column tiles.  Up to 32 rows, A is read through a
+buffer resource whose bound zero-fills the rows past M.  Every branch must meet
+the MFMA bound 4e-3 * sum_k |x*w| of the ternary GEMM ("oxibonsai-kernels 0.2.1
+-- tests_gemm_tq2.rs", correctness test) and give the same bits on a repeat.
+"""
+
+import numpy as np
+import pytest
+
+import bit_weight_gemm_amd as bw
+import oracle
+import workloads as wl
+from gpu_util import MFMA_REL, assert_within, note, run_tq2, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+# K/128 = 32 (multiple of 8: four k groups, four stages), 12 (multiple of 4 only:
+# four k groups, two stages), 6 (even: two k groups), 3 (odd: 256-column tiles)
+KS = [4096, 1536, 768, 384]
+
+
+@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("m", [1, 5, 8, 31, 32, 33, 64])
+def test_small_m_tiles_match_oracle(torch, m, k):
+    n = 1000  # 16 column tiles, the last one partial
+    aos = wl.sweep_weight(n, k)
+    x = wl.sweep_x(m, k)
+    y64, b = oracle.gemm(aos, n, k, x)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        note(f"[small-M] M={m} N={n} K={k}")
+        y = run_tq2(w, x, "mfma")
+        assert not np.isnan(y).any()
+        assert_within(y, y64, b, MFMA_REL, f"small-M M={m} K={k}")
+        again = run_tq2(w, x, "mfma")
+        assert np.array_equal(y.view(np.uint32), again.view(np.uint32)), "not deterministic"
+    finally:
+        w.close()
+
+
+def test_rows_are_independent(torch):
+    """Reversing the rows of x reverses the rows of y bit for bit (no row reads another's A)."""
+    n, k, m = 14336, 4096, 8
+    aos = wl.sweep_weight(n, k)
+    x = wl.sweep_x(m, k)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        note("[small-M] row reversal M=8 N=14336")
+        y = run_tq2(w, x, "mfma")
+        yr = run_tq2(w, x[::-1].copy(), "mfma")
+        assert np.array_equal(yr.view(np.uint32), y[::-1].view(np.uint32))
+        # a single row gives the same bits as that row inside the 8-row call
+        y1 = run_tq2(w, x[3:4].copy(), "mfma")
+        assert np.array_equal(y1.view(np.uint32), y[3:4].view(np.uint32))
+    finally:
+        w.close()
