@@ -83,11 +83,12 @@ enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2, kABuf = 3 };
 // group wk takes the 64-wide slice wk of every step, and the groups' partial
 // tiles are added through LDS at the end (wk = 0, 1, ... in order).
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool COLF, bool SCALED,
-          int EPI>
+          int EPI, int ASTG, int KSUB>
 __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) {
     constexpr int NW = WM * WN;  // waves per k group
     constexpr int T = NW * WK * 64;
-    constexpr int SK = BK * WK;  // k per step
+    constexpr int NSL = WK * KSUB;  // 64-wide k slices per step; group wk takes slices wk*KSUB ..
+    constexpr int SK = BK * NSL;    // k per step
     constexpr int NCH = SK / 8;
     constexpr int NBLK = (SK + kBlock - 1) / kBlock;  // scale blocks per step
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -95,11 +96,14 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(STAGES >= 2, "at least two pipeline stages");
     static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
+    static_assert(ASTG >= 1 && ASTG <= STAGES && BDEPTH % ASTG == 0, "A register stages");
     static_assert(AMODE != kABuf || !COLF, "buffer-loaded A has no column factors");
-    static_assert(WK == 1 || (WK - 1) * BM * BN * 4 <= STAGES * BM * SK * 2, "k-group sums must fit the A tiles");
+    // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds of MB/RED_ROUNDS row blocks
+    constexpr int RED_ROUNDS = WK == 1 ? 1 : ((WK - 1) * BM * BN * 4 + STAGES * BM * SK * 2 - 1) / (STAGES * BM * SK * 2);
+    static_assert(MB % RED_ROUNDS == 0, "k-group sums must split evenly over the rounds");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * SK];
-    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][WK][BN * 4];  // 4 code words per row and slice
+    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][NSL][BN * 4];  // 4 code words per row and slice
     __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][NBLK][BN];     // B row scales of the step
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // When there are fewer units than threads, thread t takes unit t % BITEMS
     // (duplicates load and store the same values), keeping the loop free of
     // branches; the 8-byte scale units (one row quad, one block) likewise.
-    constexpr int BITEMS = BN * WK;
+    constexpr int BITEMS = BN * NSL;
     constexpr int BPT = (BITEMS + T - 1) / T;
     static_assert(BITEMS % T == 0 || BITEMS < T, "B units: a multiple of the threads, or fewer");
     constexpr int DITEMS = (BN / 4) * NBLK;
@@ -146,8 +150,8 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     constexpr int PIECES = BM * QPR;
     constexpr int PPT = PIECES / T;
     static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
-    f4 areg[STAGES][PPT];
-    f4 creg[STAGES][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
+    f4 areg[ASTG][PPT];
+    f4 creg[ASTG][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
     u4 breg[BDEPTH][BPT];
     uint2 dreg[BDEPTH];  // scales of one row quad and block
 
@@ -196,8 +200,8 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int item = (tid + i * T) % BITEMS;
-            const int64_t quad = (n0 >> 2) + item / (4 * WK);
-            breg[st][i] = c4[quad * p.kw + (k0 >> 4) + item % (4 * WK)];
+            const int64_t quad = (n0 >> 2) + item / (4 * NSL);
+            breg[st][i] = c4[quad * p.kw + (k0 >> 4) + item % (4 * NSL)];
         }
         // whole waves past DITEMS skip the scales (a wave-uniform branch)
         if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int item = (tid + i * T) % BITEMS;
-            const int r0 = (item / (4 * WK)) * 4, g = item % (4 * WK);
+            const int r0 = (item / (4 * NSL)) * 4, g = item % (4 * NSL);
 #pragma unroll
             for (int r = 0; r < 4; ++r) Bs[st][g >> 2][b_slot(r0 + r) * 4 + (g & 3)] = breg[sb][i][r];
         }
@@ -235,45 +239,49 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         }
     };
 
-    // compute(st, hook): the MFMAs of this wave's 64-wide slice of the step in
-    // LDS buffer st; hook() runs after the first 16-wide sub-step, so the staging
-    // of the next step overlaps the remaining MFMAs of this one.
+    // compute(st, hook): the MFMAs of this wave's KSUB 64-wide slices of the step
+    // in LDS buffer st; hook() runs after the first 16-wide sub-step, so the
+    // staging of the next step overlaps the remaining MFMAs of this one.
     auto compute = [&](int st, auto &&hook) {
-        u4 bw[NB];
-        _Float16 dv[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int row = wn * WTN + nb * 32 + lrow;
-            bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][wk][b_slot(row) * 4]);
-            dv[nb] = SCALED ? Ds[st][(wk * BK) / kBlock][row] : (_Float16)1.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h8 a[MB], b[NB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int row = wm * WTM + mb * 32 + lrow;
-                a[mb] = *reinterpret_cast<const h8 *>(&As[st][lds_off<NCH>(row, wk * 8 + 2 * j + hk)]);
-            }
+        for (int ks = 0; ks < KSUB; ++ks) {
+            const int sl = wk * KSUB + ks;  // this wave's slice of the step
+            u4 bw[NB];
+            _Float16 dv[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                b[nb] = half_group_m1(bw[nb][j], hk, magic);
-                if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
+                const int row = wn * WTN + nb * 32 + lrow;
+                bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][sl][b_slot(row) * 4]);
+                dv[nb] = SCALED ? Ds[st][(sl * BK) / kBlock][row] : (_Float16)1.0f;
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int j = 0; j < 4; ++j) {
+                h8 a[MB], b[NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
-            if (j == 0) hook();
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int row = wm * WTM + mb * 32 + lrow;
+                    a[mb] = *reinterpret_cast<const h8 *>(&As[st][lds_off<NCH>(row, sl * 8 + 2 * j + hk)]);
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    b[nb] = half_group_m1(bw[nb][j], hk, magic);
+                    if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+                if (ks == 0 && j == 0) hook();
+            }
         }
     };
 
     // Pipeline: register stages hold steps loaded from memory but not yet in LDS;
     // LDS buffer t % STAGES holds step t.  While step t computes, step t+1 moves
     // from registers to LDS, and its register stages are refilled: A's with step
-    // t+1+STAGES, B's with step t+1+BDEPTH (loads issued STAGES, or BDEPTH,
-    // steps before they are stored).  One barrier per step makes step t+1's tile
+    // t+1+ASTG, B's with step t+1+BDEPTH (loads issued ASTG, or BDEPTH, steps
+    // before they are stored).  One barrier per step makes step t+1's tile
     // visible; buffer (t+1) % STAGES was last read by step t+1-STAGES <= t-1,
     // which every wave finished before the barrier that ended step t-1.  The
     // step count is a multiple of BDEPTH, so the loop is branch-free; loads and
@@ -282,12 +290,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * SK; };
 #pragma unroll
     for (int st = 0; st < BDEPTH; ++st) {
-        if (st < STAGES) load_a(st, st * SK);
+        if (st < ASTG) load_a(st, st * SK);
         load_b(st, clampk(st));
         __builtin_amdgcn_sched_barrier(0);
     }
     store(0, 0, 0);
-    load_a(0, clampk(STAGES));
+    load_a(0, clampk(ASTG));
     load_b(0, clampk(BDEPTH));
     __syncthreads();
     for (int t0 = 0; t0 < nsteps; t0 += BDEPTH) {
@@ -297,8 +305,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int nbuf = (s + 1) % STAGES;  // LDS buffer and A register stage of step t+1
             const int nsb = (s + 1) % BDEPTH;  // B register stage of step t+1
             compute(s % STAGES, [&] {
-                store(nbuf, nbuf, nsb);
-                load_a(nbuf, clampk(t + 1 + STAGES));
+                const int nsa = (s + 1) % ASTG;  // A register stage of step t+1
+                store(nbuf, nsa, nsb);
+                load_a(nsa, clampk(t + 1 + ASTG));
                 load_b(nsb, clampk(t + 1 + BDEPTH));
             });
             __syncthreads();
@@ -308,26 +317,34 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     if constexpr (WK > 1) {
         // k groups 1..WK-1 leave their partial tiles in LDS (over the A tiles,
         // which the loop no longer reads); group 0 adds them in group order.
+        // When they do not fit at once, row blocks go in rounds.
+        constexpr int MBR = MB / RED_ROUNDS;
         float *red = reinterpret_cast<float *>(&As[0][0]);
-        auto at = [&](int g, int mb, int nb, int r) { return (((g * NW + wr) * MB + mb) * NB + nb) * 1024 + r * 64 + lane; };
-        if (wk > 0) {
+        auto at = [&](int g, int mb, int nb, int r) { return (((g * NW + wr) * MBR + mb) * NB + nb) * 1024 + r * 64 + lane; };
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+        for (int ro = 0; ro < RED_ROUNDS; ++ro) {
+            if (wk > 0) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
+                for (int mb = 0; mb < MBR; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) red[at(wk - 1, mb, nb, r)] = acc[mb][nb][r];
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) red[at(wk - 1, mb, nb, r)] = acc[ro * MBR + mb][nb][r];
+            }
+            __syncthreads();
+            if (wk == 0) {
+#pragma unroll 1
+                for (int g = 1; g < WK; ++g)
+#pragma unroll
+                    for (int mb = 0; mb < MBR; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[ro * MBR + mb][nb][r] += red[at(g - 1, mb, nb, r)];
+            }
+            if (ro + 1 < RED_ROUNDS) __syncthreads();
         }
-        __syncthreads();
         if (wk > 0) return;
-#pragma unroll
-        for (int g = 1; g < WK; ++g)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mb][nb][r] += red[at(g - 1, mb, nb, r)];
     }
 
     // ---- epilogue: lane holds column lrow, rows 8*(r/4) + 4*hk + r%4 of each block
@@ -350,12 +367,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 }
 
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI,
-          int BDEPTH = STAGES>
+          int BDEPTH = STAGES, int ASTG = STAGES, int KSUB = 1>
 static hipError_t run_gemm(GemmArgs p, hipStream_t s) {
     p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
-    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, COLF, SCALED, EPI>
+    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, COLF, SCALED, EPI, ASTG, KSUB>
         <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();
 }
@@ -399,6 +416,10 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     if (M <= 64)
         return four ? run_gemm<32, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
                     : run_gemm<32, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
+    // Large M: 128 x 256 tiles of eight waves, two per SIMD: four column waves
+    // times two k groups, each k group taking one 64-wide half of a 128-wide
+    // step (two LDS buffers, one A register stage).
+    if (kb % 2 == 0) return run_gemm<128, 256, 1, 4, 2, 2, kAExact, false, true, kEpiStore, 2, 1>(p, s);
     return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
                 : run_gemm<128, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
 }
