@@ -33,7 +33,8 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 enum Epi { kEpiStore = 0, kEpiRowScale = 1 };
 
 struct GemmArgs {
-    const float *A;          // [M][lda] f32
+    const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
+    const _Float16 *Ah;      // [M][lda] f16 (kAHalf)
     int64_t lda;
     const float *colf;       // [K] per-k factor or nullptr
     const uint32_t *codes;   // [Npad][kw] code words of B
@@ -44,9 +45,11 @@ struct GemmArgs {
     int64_t ldc;
     const float *rowf;       // [N] output factor (kEpiRowScale)
     int M, N, K;             // true sizes; K bounds the A loads
-    int Kloop;               // K rounded up to a multiple of STAGES*64 (codes are padded)
+    int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
     int a_vec;               // A rows and column factors allow 16-byte loads (K % 4 == 0, aligned)
+    int64_t c_slice;         // K slices (grid.y): slice s covers k in [s*Kloop, (s+1)*Kloop) and
+                             // writes its partial product to C + s*c_slice
 };
 
 // LDS has 64 four-byte banks on gfx950: a 16-byte read serves 16 lanes per
@@ -76,8 +79,9 @@ __device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15);
 // kAScalar: element-wise guarded loads (any K).  kABuf: as kAExact, but through
 // a buffer resource spanning the M rows, so loads of rows past M return zero
 // without a memory request (small M, M*lda*4 < 2^31).  Rows past M only reach
-// output rows that are never stored.
-enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2, kABuf = 3 };
+// output rows that are never stored.  kAHalf: A already rounded to f16, K a
+// multiple of the step (zero-padded by the producer), rows past M read row M-1.
+enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2, kABuf = 3, kAHalf = 4 };
 
 // Workgroup: WK groups of WM x WN waves.  Each step covers SK = 64*WK of K; wave
 // group wk takes the 64-wide slice wk of every step, and the groups' partial
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(STAGES >= 2, "at least two pipeline stages");
     static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
     static_assert(ASTG >= 1 && ASTG <= STAGES && BDEPTH % ASTG == 0, "A register stages");
-    static_assert(AMODE != kABuf || !COLF, "buffer-loaded A has no column factors");
+    static_assert((AMODE != kABuf && AMODE != kAHalf) || !COLF, "this A mode has no column factors");
     // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds of MB/RED_ROUNDS row blocks
     constexpr int RED_ROUNDS = WK == 1 ? 1 : ((WK - 1) * BM * BN * 4 + STAGES * BM * SK * 2 - 1) / (STAGES * BM * SK * 2);
     static_assert(MB % RED_ROUNDS == 0, "k-group sums must split evenly over the rounds");
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     if ((tiles & 7) == 0) tile = (tile & 7) * (tiles >> 3) + (tile >> 3);
     const int m0 = (tile / p.tiles_n) * BM;
     const int n0 = (tile % p.tiles_n) * BN;
+    const int kbase = blockIdx.y * p.Kloop;
 
     f16x acc[MB][NB];
 #pragma unroll
@@ -143,10 +148,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(BITEMS % T == 0 || BITEMS < T, "B units: a multiple of the threads, or fewer");
     constexpr int DITEMS = (BN / 4) * NBLK;
     static_assert(DITEMS <= T && T % DITEMS == 0, "scale units must tile the threads");
-    // A is moved in 16-byte pieces (4 floats): piece q of tile row r covers
-    // k = 4q..4q+3 of the step; consecutive lanes take consecutive pieces of a
-    // row, so each wave-wide load reads whole row segments.
-    constexpr int QPR = SK / 4;  // pieces per row
+    // A is moved in 16-byte pieces (4 floats, or 8 halves for kAHalf): piece q
+    // of tile row r covers k = EPP*q .. EPP*q+EPP-1 of the step; consecutive
+    // lanes take consecutive pieces of a row, so each wave-wide load reads whole
+    // row segments.
+    constexpr int EPP = AMODE == kAHalf ? 8 : 4;  // elements per piece
+    constexpr int QPR = SK / EPP;                  // pieces per row
     constexpr int PIECES = BM * QPR;
     constexpr int PPT = PIECES / T;
     static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
@@ -164,10 +171,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int c = 0; c < PPT; ++c) {
             const int piece = tid + c * T;
             const int row = piece / QPR, q = piece % QPR;
-            const int gm = m0 + row, gk = k0 + q * 4;
+            const int gm = m0 + row, gk = k0 + q * EPP;
             // rows past M read row M-1 (valid memory); their output rows are not stored
             const int gmc = gm < p.M ? gm : p.M - 1;
-            if constexpr (AMODE == kABuf) {
+            if constexpr (AMODE == kAHalf) {
+                areg[st][c] = *reinterpret_cast<const f4 *>(p.Ah + (int64_t)gmc * p.lda + gk);  // 8 halves
+            } else if constexpr (AMODE == kABuf) {
                 areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (gm * (int)p.lda + gk) * 4, 0, 0));
             } else if constexpr (AMODE == kAExact) {
                 areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
@@ -216,15 +225,19 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int c = 0; c < PPT; ++c) {
             const int piece = tid + c * T;
             const int row = piece / QPR, q = piece % QPR;
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            h4 v;
+            if constexpr (AMODE == kAHalf) {
+                *reinterpret_cast<f4 *>(&As[st][lds_off<NCH>(row, q)]) = areg[sa][c];  // a whole 16-byte chunk
+            } else {
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                h4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float a = areg[sa][c][e];
-                if constexpr (COLF) a = a * creg[sa][c][e];  // factors past K are 0
-                v[e] = (_Float16)a;
+                for (int e = 0; e < 4; ++e) {
+                    float a = areg[sa][c][e];
+                    if constexpr (COLF) a = a * creg[sa][c][e];  // factors past K are 0
+                    v[e] = (_Float16)a;
+                }
+                *reinterpret_cast<h4 *>(&As[st][lds_off<NCH>(row, q >> 1) + ((q & 1) << 2)]) = v;
             }
-            *reinterpret_cast<h4 *>(&As[st][lds_off<NCH>(row, q >> 1) + ((q & 1) << 2)]) = v;
         }
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
@@ -287,10 +300,10 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // step count is a multiple of BDEPTH, so the loop is branch-free; loads and
     // stores past the end use clamped addresses and are never read.
     const int nsteps = p.Kloop / SK;
-    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * SK; };
+    auto clampk = [&](int t) { return kbase + (t < nsteps ? t : nsteps - 1) * SK; };
 #pragma unroll
     for (int st = 0; st < BDEPTH; ++st) {
-        if (st < ASTG) load_a(st, st * SK);
+        if (st < ASTG) load_a(st, clampk(st));
         load_b(st, clampk(st));
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -355,12 +368,13 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
             if (gn >= p.N) continue;
             const float rf = (EPI == kEpiRowScale) ? p.rowf[gn] : 1.0f;
+            float *C = p.C + blockIdx.y * p.c_slice;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (gm < p.M) {
                     const float v = acc[mb][nb][r];
-                    p.C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
+                    C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
                 }
             }
         }
@@ -368,12 +382,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI,
           int BDEPTH = STAGES, int ASTG = STAGES, int KSUB = 1>
-static hipError_t run_gemm(GemmArgs p, hipStream_t s) {
+static hipError_t run_gemm(GemmArgs p, hipStream_t s, int slices = 1) {
     p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
     mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, COLF, SCALED, EPI, ASTG, KSUB>
-        <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
+        <<<dim3((unsigned)tiles, (unsigned)slices), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -428,71 +442,159 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
 
 static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-constexpr int kBlrBN = 64;
+// Tiles of the two products.  The preparation pass re-lays both bitmaps and
+// writes f16(x*g) (the A operand of GEMM1, zero-padded in K).  GEMM1 (M x r,
+// long K = d_in) is split along K into `splits` slices whose partial products
+// go to the workspace; a small pass adds them, applies l and rounds to f16
+// (the A operand of GEMM2, M x d_out, K = r).
+constexpr int kBlr1BM = 128, kBlr1BN = 128;  // GEMM1: 4 waves of 128 x 32
+constexpr int kBlr1Step = 4 * BK;            // k per K-slice unit (4 stages of 64)
+constexpr int kBlr2Step = 2 * 2 * BK;        // GEMM2: two k groups x 64, two stages
 
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrPlan p{};
     p.M = M, p.d_in = d_in, p.d_out = d_out, p.r = r;
-    p.kpad1 = round_up(d_in, 4 * BK);  // four pipeline stages of BK
-    p.kpad2 = round_up(r, 4 * BK);
+    // K slices of GEMM1: enough workgroups to fill the chip, each slice at least one unit
+    const int64_t tiles1 = ((M + kBlr1BM - 1) / kBlr1BM) * ((r + kBlr1BN - 1) / kBlr1BN);
+    const int64_t units = (d_in + kBlr1Step - 1) / kBlr1Step;
+    int64_t sl = 1;
+    while (sl < 8 && 2 * sl <= units && tiles1 * sl < 256) sl *= 2;
+    p.splits = sl;
+    p.kchunk1 = round_up((d_in + sl - 1) / sl, kBlr1Step);
+    p.kpad1 = sl * p.kchunk1;
+    p.kpad2 = round_up(r, kBlr2Step);
     p.npad1 = round_up(r, kRowPad);
     p.npad2 = round_up(d_out, kRowPad);
     size_t off = 0;
-    p.off_codes_v = off;
-    off += (size_t)p.npad1 * (p.kpad1 / 16) * 4;
-    off = (size_t)round_up((int64_t)off, 256);
-    p.off_codes_u = off;
-    off += (size_t)p.npad2 * (p.kpad2 / 16) * 4;
-    off = (size_t)round_up((int64_t)off, 256);
-    p.off_a = off;
-    off += (size_t)M * r * 4;
-    p.total = (size_t)round_up((int64_t)off, 256);
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return at;
+    };
+    p.off_codes_v = take((size_t)p.npad1 * (p.kpad1 / 16) * 4);
+    p.off_codes_u = take((size_t)p.npad2 * (p.kpad2 / 16) * 4);
+    p.off_part = take((size_t)p.splits * M * r * 4);
+    p.off_al = take((size_t)M * p.kpad2 * 2);
+    p.off_xg = take((size_t)M * p.kpad1 * 2);
+    p.total = off;
     return p;
 }
 
 // Sign bitmaps -> code words (set bit -> code 2 = +1, clear -> code 0 = -1,
-// padding -> code 1 = 0) in the device layout, with row index `n` and
-// contraction index `k`:
-//   S_U: sign(n, k) = bit k of bits[n][k/32]   (n = output i, k = rank): one
-//        thread per output word, reading half a bitmap word;
-//   S_V: sign(n, k) = bit n of bits[k][n/32]   (n = rank, k = input j): a wave
-//        covers 64 consecutive ranks of one 16-wide k group, so each of its 16
-//        loads touches two bitmap words shared by all lanes.
-__global__ __launch_bounds__(256) void bits_u_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
-                                                              uint32_t *__restrict__ codes, int64_t n_real,
-                                                              int64_t k_real, int64_t n_pad, int64_t k_pad) {
-    const int64_t kw = k_pad / 16;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= n_pad * kw) return;
-    const int64_t n = gid / kw, g = gid % kw;  // reads along the bitmap row
-    uint32_t half = 0;
-    if (n < n_real && g * 16 < k_real) half = (bits[n * words + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu;
-    uint32_t out = 0;
+// padding -> code 1 = 0) in the device layout, with row index n and
+// contraction index k, for both matrices in one launch.  A thread makes the
+// 16-byte unit of four rows (4q .. 4q+3) for one 16-wide k group g.
+//   S_V: sign(n, k) = bit n of bits_v[k][n/32]   (n = rank, k = input j): a wave
+//        takes 64 consecutive row quads of one group, so each of its 16 loads
+//        (one per k) touches 8 bitmap words shared by the lanes;
+//   S_U: sign(n, k) = bit k of bits_u[n][k/32]   (n = output i, k = rank): a
+//        wave takes 64 consecutive groups of one row quad, so its loads read
+//        whole bitmap rows and its stores are contiguous.
+// Out-of-range elements read a valid word and are replaced by code 1.
+// Blocks from nblk_v + nblk_u on write xg[m][k] = f16(x[m][k] * g[k]) (product in
+// f32, round to nearest even) for k < d_in and 0 up to kpad1, 8 values per thread.
+struct BlrPrep {
+    const uint32_t *bits_v, *bits_u;
+    uint32_t *codes_v, *codes_u;
+    const float *x, *g;
+    _Float16 *xg;
+    int64_t words;                     // r / 32
+    int64_t M, r, d_in, d_out;
+    int64_t npad1, kpad1, npad2, kpad2;
+    int64_t nblk_v, nblk_u;
+    int xvec;                          // x rows and g allow 16-byte loads
+};
+
+// code of element e (0..15) at its place in a group word
+__device__ __forceinline__ uint32_t code_at(uint32_t code, int e) { return code << (2 * (e >> 1) + 16 * (e & 1)); }
+
+__global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
+    const int64_t bid = blockIdx.x;
+    if (bid < q.nblk_v) {
+        const int64_t kw = q.kpad1 / 16, quads = q.npad1 / 4;
+        const int64_t qblocks = (quads + 255) / 256;
+        const int64_t quad = (bid % qblocks) * 256 + threadIdx.x, g = bid / qblocks;
+        if (quad >= quads) return;
+        const int64_t n0 = quad * 4;
+        const bool nin = n0 < q.r;  // r % 32 == 0: a quad is wholly inside or wholly past r
+        const int64_t wrd = nin ? n0 >> 5 : 0;
+        const int sh = (int)(n0 & 31);
+        u4 out = {0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int64_t k = g * 16 + e;
-        const uint32_t code = (n < n_real && k < k_real) ? (((half >> e) & 1u) ? 2u : 0u) : 1u;
-        out |= code << (2 * (e >> 1) + 16 * (e & 1));
+        for (int e = 0; e < 16; ++e) {
+            const int64_t k = g * 16 + e;
+            const bool in = nin && k < q.d_in;
+            const uint32_t bits = (q.bits_v[(in ? k : 0) * q.words + wrd] >> sh) & 15u;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                out[rr] |= code_at(in ? (((bits >> rr) & 1u) ? 2u : 0u) : 1u, e);
+        }
+        *reinterpret_cast<u4 *>(q.codes_v + (quad * kw + g) * 4) = out;
+    } else if (bid < q.nblk_v + q.nblk_u) {
+        const int64_t kw = q.kpad2 / 16;
+        const int64_t gblocks = (kw + 255) / 256;
+        const int64_t rel = bid - q.nblk_v;
+        const int64_t quad = rel / gblocks, g = (rel % gblocks) * 256 + threadIdx.x;
+        if (g >= kw) return;
+        u4 out;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t n = quad * 4 + rr;
+            const bool in = n < q.d_out && g * 16 < q.r;
+            const uint32_t half = (q.bits_u[(in ? n : 0) * q.words + (in ? g >> 1 : 0)] >> (16 * (g & 1))) & 0xFFFFu;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const bool ine = in && g * 16 + e < q.r;
+                w |= code_at(ine ? (((half >> e) & 1u) ? 2u : 0u) : 1u, e);
+            }
+            out[rr] = w;
+        }
+        *reinterpret_cast<u4 *>(q.codes_u + (quad * kw + g) * 4) = out;
+    } else {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const int64_t per_row = q.kpad1 / 8;
+        const int64_t piece = (bid - q.nblk_v - q.nblk_u) * 256 + threadIdx.x;
+        if (piece >= q.M * per_row) return;
+        const int64_t m = piece / per_row, k0 = (piece % per_row) * 8;
+        const float *xr = q.x + m * q.d_in;
+        h8 out;
+        if (q.xvec && k0 + 8 <= q.d_in) {
+            const f4 x0 = *reinterpret_cast<const f4 *>(xr + k0), x1 = *reinterpret_cast<const f4 *>(xr + k0 + 4);
+            const f4 g0 = *reinterpret_cast<const f4 *>(q.g + k0), g1 = *reinterpret_cast<const f4 *>(q.g + k0 + 4);
+            const f4 p0 = x0 * g0, p1 = x1 * g1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (_Float16)p0[e], out[e + 4] = (_Float16)p1[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t k = k0 + e;
+                out[e] = (_Float16)(k < q.d_in ? xr[k] * q.g[k] : 0.0f);
+            }
+        }
+        *reinterpret_cast<h8 *>(q.xg + m * q.kpad1 + k0) = out;
     }
-    codes[code_index(n, g, kw)] = out;
 }
 
-__global__ __launch_bounds__(256) void bits_v_to_codes_kernel(const uint32_t *__restrict__ bits, int64_t words,
-                                                              uint32_t *__restrict__ codes, int64_t n_real,
-                                                              int64_t k_real, int64_t n_pad, int64_t k_pad) {
-    const int64_t kw = k_pad / 16;
-    const int64_t n = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-    const int64_t g = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (n >= n_pad || g >= kw) return;
-    uint32_t out = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int64_t k = g * 16 + e;
-        uint32_t code = 1;
-        if (n < n_real && k < k_real) code = ((bits[k * words + (n >> 5)] >> (n & 31)) & 1u) ? 2u : 0u;
-        out |= code << (2 * (e >> 1) + 16 * (e & 1));
+// al[m][k] = f16(l[k] * sum_s part[s][m][k]) for k < r (slices added in order,
+// product in f32, round to nearest even), 0 up to kpad2; four values per thread.
+__global__ __launch_bounds__(256) void blr_mid_kernel(const float *__restrict__ part, const float *__restrict__ l,
+                                                      _Float16 *__restrict__ al, int64_t M, int64_t r, int64_t kpad2,
+                                                      int splits) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // piece of 4 along [M][kpad2]
+    const int64_t per_row = kpad2 / 4;
+    if (q >= M * per_row) return;
+    const int64_t m = q / per_row, k = (q % per_row) * 4;
+    f4 v = {};
+    if (k < r) {  // r % 32 == 0: a piece is wholly inside or wholly past r
+        for (int sl = 0; sl < splits; ++sl) {
+            const f4 t = *reinterpret_cast<const f4 *>(part + ((int64_t)sl * M + m) * r + k);
+            v = sl == 0 ? t : v + t;
+        }
+        v *= f4{l[k], l[k + 1], l[k + 2], l[k + 3]};  // l is only 4-byte aligned
     }
-    codes[code_index(n, g, kw)] = out;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<h4 *>(al + m * kpad2 + k) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
 }
 
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
@@ -501,39 +603,48 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     char *ws = static_cast<char *>(workspace);
     uint32_t *codes_v = reinterpret_cast<uint32_t *>(ws + pl.off_codes_v);
     uint32_t *codes_u = reinterpret_cast<uint32_t *>(ws + pl.off_codes_u);
-    float *a = reinterpret_cast<float *>(ws + pl.off_a);
-    const int64_t words = pl.r / 32;
-
+    float *part = reinterpret_cast<float *>(ws + pl.off_part);
+    _Float16 *al = reinterpret_cast<_Float16 *>(ws + pl.off_al);
+    _Float16 *xg = reinterpret_cast<_Float16 *>(ws + pl.off_xg);
     {
-        const dim3 gv((unsigned)(pl.npad1 / 64), (unsigned)((pl.kpad1 / 16 + 3) / 4));
-        bits_v_to_codes_kernel<<<gv, dim3(256), 0, s>>>(bits_v, words, codes_v, pl.r, pl.d_in, pl.npad1, pl.kpad1);
-        const int64_t tot2 = pl.npad2 * (pl.kpad2 / 16);
-        bits_u_to_codes_kernel<<<dim3((unsigned)((tot2 + 255) / 256)), dim3(256), 0, s>>>(
-            bits_u, words, codes_u, pl.d_out, pl.r, pl.npad2, pl.kpad2);
+        BlrPrep q{};
+        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
+        q.x = x, q.g = g, q.xg = xg;
+        q.words = pl.r / 32, q.M = pl.M, q.r = pl.r, q.d_in = pl.d_in, q.d_out = pl.d_out;
+        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
+        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
+        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.xvec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+        const int64_t nblk_x = (pl.M * (pl.kpad1 / 8) + 255) / 256;
+        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // GEMM1: a[M][r] = f16(x.g) . S_V
+    // GEMM1: part[s][M][r] = xg[:, slice s] . S_V[slice s, :]
     GemmArgs p1{};
-    p1.A = x, p1.lda = pl.d_in, p1.colf = g;
+    p1.Ah = xg, p1.lda = pl.kpad1;
     p1.codes = codes_v, p1.kw = pl.kpad1 / 16, p1.scales = nullptr, p1.kbw = 0;
-    p1.C = a, p1.ldc = pl.r, p1.rowf = nullptr;
-    p1.M = (int)pl.M, p1.N = (int)pl.r, p1.K = (int)pl.d_in, p1.Kloop = (int)pl.kpad1;
-    p1.a_vec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-               ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
-    hipError_t e = p1.a_vec ? run_gemm<64, kBlrBN, 2, 2, 1, 4, kAVec, true, false, kEpiStore>(p1, s)
-                            : run_gemm<64, kBlrBN, 2, 2, 1, 4, kAScalar, true, false, kEpiStore>(p1, s);
+    p1.C = part, p1.ldc = pl.r, p1.rowf = nullptr, p1.c_slice = pl.M * pl.r;
+    p1.M = (int)pl.M, p1.N = (int)pl.r, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kchunk1;
+    const int sl = (int)pl.splits;
+    hipError_t e = run_gemm<kBlr1BM, kBlr1BN, 1, 4, 1, 4, kAHalf, false, false, kEpiStore>(p1, s, sl);
     if (e != hipSuccess) return e;
-    // GEMM2: y[M][d_out] = h . (f16(a.l) . S_U^T)
+    {
+        const int64_t pieces = pl.M * (pl.kpad2 / 4);
+        blr_mid_kernel<<<dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s>>>(part, l, al, pl.M, pl.r,
+                                                                                    pl.kpad2, sl);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // GEMM2: y[M][d_out] = h . (al . S_U^T)
     GemmArgs p2{};
-    p2.A = a, p2.lda = pl.r, p2.colf = l;
+    p2.Ah = al, p2.lda = pl.kpad2, p2.colf = nullptr;
     p2.codes = codes_u, p2.kw = pl.kpad2 / 16, p2.scales = nullptr, p2.kbw = 0;
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
-    p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.r, p2.Kloop = (int)pl.kpad2;
-    // a is the 256-byte aligned workspace and r % 32 == 0; l decides
-    p2.a_vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
-    return p2.a_vec ? run_gemm<64, kBlrBN, 2, 2, 1, 4, kAVec, true, false, kEpiRowScale>(p2, s)
-                    : run_gemm<64, kBlrBN, 2, 2, 1, 4, kAScalar, true, false, kEpiRowScale>(p2, s);
+    p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.kpad2, p2.Kloop = (int)pl.kpad2;
+    p2.a_vec = 1;
+    return run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScale, 2, 1>(p2, s);
 }
 
 }  // namespace tq2
