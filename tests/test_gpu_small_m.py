@@ -1,12 +1,14 @@
-"""GPU parity of the MFMA path's small-M tiles with the oracle.
+"""GPU parity of the MFMA path's small-M kernels with the oracle.
 
-For M <= 64 the MFMA path uses 64-column tiles whose waves split each step's K
-range (four ways when the block count K/128 is a multiple of 4, two ways when
-it is even) and add their partial tiles in a fixed order at the end; an odd
-block count takes the 256-column tiles.  Up to 32 rows, A is read through a
-buffer resource whose bound zero-fills the rows past M.  Every branch must meet
-the MFMA bound 4e-3 * sum_k |x*w| of the ternary GEMM ("oxibonsai-kernels 0.2.1
--- tests_gemm_tq2.rs", correctness test) and give the same bits on a repeat.
+Up to 16 rows (with M*K <= 32768) the MFMA path runs the skinny kernel: x is
+staged whole in LDS and eight waves each take one eighth of K, their partial
+tiles added in wave order.  Other M <= 32 take 32x64 tiles whose waves split
+each step's K range (four ways when the block count K/128 is a multiple of 4,
+two ways when it is even) and read A through a buffer resource whose bound
+zero-fills the rows past M; 33 <= M <= 64 take 64x64 tiles; an odd block count
+takes the 256-column tiles.  Every branch must meet the MFMA bound
+4e-3 * sum_k |x*w| of the ternary GEMM ("oxibonsai-kernels 0.2.1 --
+tests_gemm_tq2.rs", correctness test) and give the same bits on a repeat.
 """
 
 import numpy as np
@@ -26,7 +28,9 @@ def torch():
 
 
 # K/128 = 32 (multiple of 8: four k groups, four stages), 12 (multiple of 4 only:
-# four k groups, two stages), 6 (even: two k groups), 3 (odd: 256-column tiles)
+# four k groups, two stages), 6 (even: two k groups), 3 (odd: 256-column tiles).
+# Of these only K=4096 and 1536 give K % 512 == 0, so M <= 16 (and M*K <= 32768)
+# runs the skinny kernel there and the tiled kernels otherwise.
 KS = [4096, 1536, 768, 384]
 
 
