@@ -54,10 +54,9 @@ hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M
 // Binary low-rank forward.  Workspace carve-up is computed by blr_plan.
 struct BlrPlan {
     int64_t M, d_in, d_out, r;
-    int64_t splits, kchunk1;     // GEMM1's K slices and the padded k range of each
-    int64_t kpad1, kpad2;        // contraction lengths of GEMM1 (splits*kchunk1) and GEMM2 (r, padded)
+    int64_t kpad1, kpad2;        // contraction lengths of GEMM1 (d_in, padded) and GEMM2 (r, padded)
     int64_t npad1, npad2;        // padded output widths of GEMM1 (r) and GEMM2 (d_out)
-    size_t off_codes_v, off_codes_u, off_part, off_al, off_xg, total;
+    size_t off_codes_v, off_codes_u, off_al, off_xg, total;
 };
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 hipError_t launch_blr_forward(const BlrPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,

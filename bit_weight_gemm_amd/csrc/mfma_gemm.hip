@@ -30,7 +30,10 @@ constexpr int BK = 64;
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-enum Epi { kEpiStore = 0, kEpiRowScale = 1 };
+// Epilogues: plain f32 store; f32 store times a factor per output column;
+// f16 store (round to nearest even) of the product with a factor per column,
+// 0 past the first nrowf columns.
+enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2 };
 
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
@@ -42,8 +45,10 @@ struct GemmArgs {
     const uint16_t *scales;  // [Npad][kbw] f16 scales of B, or nullptr
     int64_t kbw;
     float *C;                // [M][ldc]
+    _Float16 *Ch;            // [M][ldc] (kEpiHalfScale)
     int64_t ldc;
-    const float *rowf;       // [N] output factor (kEpiRowScale)
+    const float *rowf;       // [N] output factor (kEpiRowScale, kEpiHalfScale)
+    int nrowf;               // factors present (kEpiHalfScale: columns past it get 0)
     int M, N, K;             // true sizes; K bounds the A loads
     int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
@@ -102,9 +107,10 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
     static_assert(ASTG >= 1 && ASTG <= STAGES && BDEPTH % ASTG == 0, "A register stages");
     static_assert((AMODE != kABuf && AMODE != kAHalf) || !COLF, "this A mode has no column factors");
-    // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds of MB/RED_ROUNDS row blocks
+    // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds, each taking
+    // an equal share of the wave's MB x NB accumulator blocks
     constexpr int RED_ROUNDS = WK == 1 ? 1 : ((WK - 1) * BM * BN * 4 + STAGES * BM * SK * 2 - 1) / (STAGES * BM * SK * 2);
-    static_assert(MB % RED_ROUNDS == 0, "k-group sums must split evenly over the rounds");
+    static_assert((MB * NB) % RED_ROUNDS == 0, "k-group sums must split evenly over the rounds");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * SK];
     __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][NSL][BN * 4];  // 4 code words per row and slice
@@ -330,30 +336,30 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     if constexpr (WK > 1) {
         // k groups 1..WK-1 leave their partial tiles in LDS (over the A tiles,
         // which the loop no longer reads); group 0 adds them in group order.
-        // When they do not fit at once, row blocks go in rounds.
-        constexpr int MBR = MB / RED_ROUNDS;
+        // When they do not fit at once, accumulator blocks go in rounds.
+        constexpr int BPR = MB * NB / RED_ROUNDS;  // accumulator blocks per round
         float *red = reinterpret_cast<float *>(&As[0][0]);
-        auto at = [&](int g, int mb, int nb, int r) { return (((g * NW + wr) * MBR + mb) * NB + nb) * 1024 + r * 64 + lane; };
+        auto at = [&](int g, int i, int r) { return ((g * NW + wr) * BPR + i) * 1024 + r * 64 + lane; };
 #pragma unroll
         for (int ro = 0; ro < RED_ROUNDS; ++ro) {
             if (wk > 0) {
 #pragma unroll
-                for (int mb = 0; mb < MBR; ++mb)
+                for (int i = 0; i < BPR; ++i) {
+                    const int blk = ro * BPR + i;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) red[at(wk - 1, mb, nb, r)] = acc[ro * MBR + mb][nb][r];
+                    for (int r = 0; r < 16; ++r) red[at(wk - 1, i, r)] = acc[blk / NB][blk % NB][r];
+                }
             }
             __syncthreads();
             if (wk == 0) {
 #pragma unroll 1
                 for (int g = 1; g < WK; ++g)
 #pragma unroll
-                    for (int mb = 0; mb < MBR; ++mb)
+                    for (int i = 0; i < BPR; ++i) {
+                        const int blk = ro * BPR + i;
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[ro * MBR + mb][nb][r] += red[at(g - 1, mb, nb, r)];
+                        for (int r = 0; r < 16; ++r) acc[blk / NB][blk % NB][r] += red[at(g - 1, i, r)];
+                    }
             }
             if (ro + 1 < RED_ROUNDS) __syncthreads();
         }
@@ -367,14 +373,19 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int nb = 0; nb < NB; ++nb) {
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
             if (gn >= p.N) continue;
-            const float rf = (EPI == kEpiRowScale) ? p.rowf[gn] : 1.0f;
+            float rf = 1.0f;
+            if constexpr (EPI == kEpiRowScale) rf = p.rowf[gn];
+            if constexpr (EPI == kEpiHalfScale) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
             float *C = p.C + blockIdx.y * p.c_slice;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (gm < p.M) {
                     const float v = acc[mb][nb][r];
-                    C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
+                    if constexpr (EPI == kEpiHalfScale)
+                        p.Ch[(int64_t)gm * p.ldc + gn] = (_Float16)(rf * v);
+                    else
+                        C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
                 }
             }
         }
@@ -444,24 +455,19 @@ static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Tiles of the two products.  The preparation pass re-lays both bitmaps and
 // writes f16(x*g) (the A operand of GEMM1, zero-padded in K).  GEMM1 (M x r,
-// long K = d_in) is split along K into `splits` slices whose partial products
-// go to the workspace; a small pass adds them, applies l and rounds to f16
-// (the A operand of GEMM2, M x d_out, K = r).
-constexpr int kBlr1BM = 128, kBlr1BN = 128;  // GEMM1: 4 waves of 128 x 32
-constexpr int kBlr1Step = 4 * BK;            // k per K-slice unit (4 stages of 64)
-constexpr int kBlr2Step = 2 * 2 * BK;        // GEMM2: two k groups x 64, two stages
+// K = d_in) writes f16(l * a), the A operand of GEMM2 (M x d_out, K = r), from
+// its epilogue; its columns past r are zero.  Small M takes 32 x 64 tiles of
+// GEMM1 (eight waves, four k groups) so that enough workgroups stream the long
+// K without splitting it; larger M takes 128 x 128 tiles.
+constexpr int kBlrKPad = 512;     // GEMM1's K padding: whole pipeline rounds of either tile
+constexpr int kBlr2Step = 2 * 2 * BK;  // GEMM2: two k groups x 64, two stages
+
+static bool blr_small_tiles(int64_t M, int64_t kpad2) { return ((M + 31) / 32) * (kpad2 / 64) < 2048; }
 
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrPlan p{};
     p.M = M, p.d_in = d_in, p.d_out = d_out, p.r = r;
-    // K slices of GEMM1: enough workgroups to fill the chip, each slice at least one unit
-    const int64_t tiles1 = ((M + kBlr1BM - 1) / kBlr1BM) * ((r + kBlr1BN - 1) / kBlr1BN);
-    const int64_t units = (d_in + kBlr1Step - 1) / kBlr1Step;
-    int64_t sl = 1;
-    while (sl < 8 && 2 * sl <= units && tiles1 * sl < 256) sl *= 2;
-    p.splits = sl;
-    p.kchunk1 = round_up((d_in + sl - 1) / sl, kBlr1Step);
-    p.kpad1 = sl * p.kchunk1;
+    p.kpad1 = round_up(d_in, kBlrKPad);
     p.kpad2 = round_up(r, kBlr2Step);
     p.npad1 = round_up(r, kRowPad);
     p.npad2 = round_up(d_out, kRowPad);
@@ -473,7 +479,6 @@ BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     };
     p.off_codes_v = take((size_t)p.npad1 * (p.kpad1 / 16) * 4);
     p.off_codes_u = take((size_t)p.npad2 * (p.kpad2 / 16) * 4);
-    p.off_part = take((size_t)p.splits * M * r * 4);
     p.off_al = take((size_t)M * p.kpad2 * 2);
     p.off_xg = take((size_t)M * p.kpad1 * 2);
     p.total = off;
@@ -576,34 +581,12 @@ __global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
     }
 }
 
-// al[m][k] = f16(l[k] * sum_s part[s][m][k]) for k < r (slices added in order,
-// product in f32, round to nearest even), 0 up to kpad2; four values per thread.
-__global__ __launch_bounds__(256) void blr_mid_kernel(const float *__restrict__ part, const float *__restrict__ l,
-                                                      _Float16 *__restrict__ al, int64_t M, int64_t r, int64_t kpad2,
-                                                      int splits) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // piece of 4 along [M][kpad2]
-    const int64_t per_row = kpad2 / 4;
-    if (q >= M * per_row) return;
-    const int64_t m = q / per_row, k = (q % per_row) * 4;
-    f4 v = {};
-    if (k < r) {  // r % 32 == 0: a piece is wholly inside or wholly past r
-        for (int sl = 0; sl < splits; ++sl) {
-            const f4 t = *reinterpret_cast<const f4 *>(part + ((int64_t)sl * M + m) * r + k);
-            v = sl == 0 ? t : v + t;
-        }
-        v *= f4{l[k], l[k + 1], l[k + 2], l[k + 3]};  // l is only 4-byte aligned
-    }
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<h4 *>(al + m * kpad2 + k) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-}
-
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
                               void *workspace, hipStream_t s) {
     char *ws = static_cast<char *>(workspace);
     uint32_t *codes_v = reinterpret_cast<uint32_t *>(ws + pl.off_codes_v);
     uint32_t *codes_u = reinterpret_cast<uint32_t *>(ws + pl.off_codes_u);
-    float *part = reinterpret_cast<float *>(ws + pl.off_part);
     _Float16 *al = reinterpret_cast<_Float16 *>(ws + pl.off_al);
     _Float16 *xg = reinterpret_cast<_Float16 *>(ws + pl.off_xg);
     {
@@ -621,22 +604,21 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // GEMM1: part[s][M][r] = xg[:, slice s] . S_V[slice s, :]
+    // GEMM1: al[M][kpad2] = f16(l . (xg . S_V)); rows of S_V past r are code 1, so
+    // the padded columns come out as 0 (and their factor is 0)
     GemmArgs p1{};
     p1.Ah = xg, p1.lda = pl.kpad1;
     p1.codes = codes_v, p1.kw = pl.kpad1 / 16, p1.scales = nullptr, p1.kbw = 0;
-    p1.C = part, p1.ldc = pl.r, p1.rowf = nullptr, p1.c_slice = pl.M * pl.r;
-    p1.M = (int)pl.M, p1.N = (int)pl.r, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kchunk1;
-    const int sl = (int)pl.splits;
-    hipError_t e = run_gemm<kBlr1BM, kBlr1BN, 1, 4, 1, 4, kAHalf, false, false, kEpiStore>(p1, s, sl);
-    if (e != hipSuccess) return e;
-    {
-        const int64_t pieces = pl.M * (pl.kpad2 / 4);
-        blr_mid_kernel<<<dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s>>>(part, l, al, pl.M, pl.r,
-                                                                                    pl.kpad2, sl);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    p1.Ch = al, p1.ldc = pl.kpad2, p1.rowf = l, p1.nrowf = (int)pl.r;
+    p1.M = (int)pl.M, p1.N = (int)pl.kpad2, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kpad1;
+    hipError_t e;
+    if (blr_small_tiles(pl.M, pl.kpad2)) {
+        e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiHalfScale>(p1, s)
+                                      : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiHalfScale>(p1, s);
+    } else {
+        e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiHalfScale>(p1, s);
     }
+    if (e != hipSuccess) return e;
     // GEMM2: y[M][d_out] = h . (al . S_U^T)
     GemmArgs p2{};
     p2.Ah = al, p2.lda = pl.kpad2, p2.colf = nullptr;
