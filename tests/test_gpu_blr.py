@@ -73,6 +73,11 @@ def test_blr_ragged_shapes(torch, m, d_in, d_out, r):
     _check(wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=20 + m), f"ragged {m}x{d_in}x{d_out}x{r}")
 
 
+def test_blr_many_tokens(torch):
+    """Enough tokens that the first product takes its large tiles (4100 x 1024 outputs)."""
+    _check(wl.blr_inputs(m=4100, d_in=256, d_out=96, r=1024, index=41), "many tokens", count=2048)
+
+
 def _exact_grid(m, d_in, d_out, r, seed):
     """Inputs on which every f16 operand and every f32 partial sum is exact.
 

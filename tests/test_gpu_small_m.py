@@ -2,13 +2,15 @@
 
 Up to 16 rows (with M*K <= 32768) the MFMA path runs the skinny kernel: x is
 staged whole in LDS and eight waves each take one eighth of K, their partial
-tiles added in wave order.  Other M <= 32 take 32x64 tiles whose waves split
-each step's K range (four ways when the block count K/128 is a multiple of 4,
-two ways when it is even) and read A through a buffer resource whose bound
-zero-fills the rows past M; 33 <= M <= 64 take 64x64 tiles; an odd block count
-takes the 256-column tiles.  Every branch must meet the MFMA bound
-4e-3 * sum_k |x*w| of the ternary GEMM ("oxibonsai-kernels 0.2.1 --
-tests_gemm_tq2.rs", correctness test) and give the same bits on a repeat.
+tiles added in wave order.  Other M <= 32 take 32x64 tiles and 33 <= M <= 64
+take 64x64 tiles, whose waves split each step's K (four ways; with K/128 a
+multiple of 8, each of the four takes two 64-wide slices of a 512-wide step;
+two ways when K has few blocks) and add their partial tiles in a fixed order at
+the end.  Up to 32 rows, A is read through a buffer resource whose bound
+zero-fills the rows past M.  An odd block count takes the 256-column tiles.
+Every branch must meet the MFMA bound 4e-3 * sum_k |x*w| of the ternary GEMM
+("oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs", correctness test) and give
+the same bits on a repeat.
 """
 
 import numpy as np
@@ -27,15 +29,15 @@ def torch():
     return torch_cuda()
 
 
-# K/128 = 32 (multiple of 8: four k groups, four stages), 12 (multiple of 4 only:
-# four k groups, two stages), 6 (even: two k groups), 3 (odd: 256-column tiles).
-# Of these only K=4096 and 1536 give K % 512 == 0, so M <= 16 (and M*K <= 32768)
+# K/128 = 32 (multiple of 8: four k groups of two slices), 12 (multiple of 4
+# only: four k groups), 6 (even: two k groups), 3 (odd: 256-column tiles).  Of
+# these only K=4096 and 1536 give K % 512 == 0, so M <= 16 (and M*K <= 32768)
 # runs the skinny kernel there and the tiled kernels otherwise.
 KS = [4096, 1536, 768, 384]
 
 
 @pytest.mark.parametrize("k", KS)
-@pytest.mark.parametrize("m", [1, 5, 8, 31, 32, 33, 64])
+@pytest.mark.parametrize("m", [1, 5, 8, 16, 31, 32, 33, 64])
 def test_small_m_tiles_match_oracle(torch, m, k):
     n = 1000  # 16 column tiles, the last one partial
     aos = wl.sweep_weight(n, k)
