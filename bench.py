@@ -86,9 +86,8 @@ class Timer:
     on the launch stream and by device synchronisations.  The per-step time is
     the median replay / K (the minimum is reported too).  The graph removes host
     launch cost from the timed region; every step is still one library call (one
-    or more kernel launches).  Warmup, capture and replays use one stream, so
-    per-stream library state (the split-K scratch) exists before the capture.
-    The same K steps issued eagerly from Python are timed too, as context."""
+    or more kernel launches).  Warmup, capture and replays use one stream.  The
+    same K steps issued eagerly from Python are timed too, as context."""
 
     REPS = 11
 
@@ -196,6 +195,38 @@ def bench_blr(torch, bw, steps, warmup):
     flop = 2.0 * m * r * (d_in + d_out)
     t.update(flop_per_call=flop, tflops_step=flop / (t["step_ms"] * 1e-3) / 1e12)
     return t
+
+
+def context_floors(torch, steps=500):
+    """What the box itself allows, measured the same way as the workloads: the
+    per-launch cost of a one-element fill kernel in a replayed graph, and the
+    HBM rates of a 1 GiB sum (read) and a 256 MiB copy (read + write)."""
+    tiny = torch.zeros(1, device="cuda")
+    t = Timer(torch).run(lambda i: tiny.fill_(float(i & 1)), steps, 10)
+    big = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+
+    def rate(fn, nbytes, reps=7):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return nbytes / (float(np.median(times)) * 1e-3) / 1e9
+
+    read = rate(lambda: big.sum(), big.numel() * 4)
+    copy = rate(lambda: b.copy_(a), 2 * CALIB_BYTES)
+    del big, a, b
+    return {"launch_floor_us": round(t["step_ms"] * 1e3, 3),
+            "hbm_read_gbs": round(read, 1), "hbm_copy_gbs": round(copy, 1),
+            "note": "launch floor: graph-replayed one-element fill; read: torch sum over 1 GiB f32; "
+                    "copy: 256 MiB device copy, bytes read + written"}
 
 
 def calib_copy(torch, reps=5):
@@ -382,10 +413,12 @@ def main():
                      "hbm_frac": round(v["gbs_step"] / HBM_PEAK_GBS, 4)}
     if "blr" in out:
         b = out["blr"]
-        line["blr"] = {"workload": "blr_forward M=512, d_in=d_out=4096, r=1024 (4 launches per call)",
+        line["blr"] = {"workload": "blr_forward M=512, d_in=d_out=4096, r=1024 (3 launches per call)",
                        "tflops": round(b["tflops_step"], 2), "ms_per_call": b["step_ms"],
                        "ms_per_call_min": b["step_ms_min"],
                        "mfma_frac": round(b["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4)}
+    if "decode" in only:
+        line["context"] = context_floors(torch)
     if "cpu" in only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
