@@ -4,9 +4,10 @@ Headline: weight-GB/s of tq2_gemm at M=1 (decode GEMV, N=K=4096), i.e. packed
 weight bytes (N*K/128*34) per call over the per-call time, with every call
 reading a different uploaded copy of the weight (more copies than the 256 MB
 Infinity Cache holds, so each call streams from HBM).  The same JSON line also
-reports the M=2048 prefill TFLOP/s, the small-batch MLP up-projection and the
-BLR layer forward, each with its roofline fraction, and the CPU oracle timed on
-this host's cores on a bounded sample.
+reports the M=2048 prefill TFLOP/s, the small-batch MLP up-projection, the two
+DiT benchmark shapes and the BLR layer forward, each with its roofline fraction,
+the launch and HBM floors of the box, and the CPU oracle timed on this host's
+cores on a bounded sample.
 
 Timing: W untimed warmup steps, then exactly K steps between two device
 synchronisations.  The K steps are captured once in a HIP graph and replayed, so
@@ -14,7 +15,7 @@ the timed region holds GPU work only (host launch cost removed); HIP events on
 the launch stream bracket the replay.  Each step is one library call.  The same
 K steps issued eagerly from Python are also timed and reported as context.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mlp,blr]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mlp,dit,blr,cpu]
 """
 
 from __future__ import annotations
@@ -156,6 +157,20 @@ def bench_decode(torch, bw, steps, warmup, path):
 def bench_prefill(torch, bw, steps, warmup):
     aos, x_np = wl.prefill_inputs()
     m, n, k = wl.PREFILL["M"], wl.PREFILL["N"], wl.PREFILL["K"]
+    w = bw.tq2_upload(aos, n, k)
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((m, n), device="cuda")
+    t = Timer(torch).run(lambda i: bw.tq2_gemm_path(w, x, y, bw.TQ2_PATH_MFMA), steps, warmup)
+    w.close()
+    flop = 2.0 * m * n * k
+    t.update(flop_per_call=flop, tflops_step=flop / (t["step_ms"] * 1e-3) / 1e12)
+    return t
+
+
+def bench_dit(torch, bw, steps, warmup, m, n, k):
+    """The DiT benchmark shapes of "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs" on the MFMA
+    path (LCG weights, scale 0.0625)."""
+    aos, x_np = wl.dit_weight(n, k), wl.dit_x(m, k)
     w = bw.tq2_upload(aos, n, k)
     x = torch.from_numpy(x_np).cuda()
     y = torch.empty((m, n), device="cuda")
@@ -322,7 +337,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--only", default="decode,prefill,mlp,blr,cpu")
+    ap.add_argument("--only", default="decode,prefill,mlp,dit,blr,cpu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
@@ -366,6 +381,10 @@ def main():
             for name, path in (("f32", bw.TQ2_PATH_F32), ("mfma", bw.TQ2_PATH_MFMA)):
                 out[f"mlp_m{m}_{name}"] = bench_mlp(torch, bw, max(K // 10, 20), max(W // 5, 5), m, path)
                 log(f"[mlp M={m} {name}] {json.dumps(out[f'mlp_m{m}_{name}'])}")
+    if "dit" in only:
+        for (m, n, k) in wl.DIT_SHAPES:
+            out[f"dit_{m}x{n}x{k}"] = bench_dit(torch, bw, max(K // 100, 10), 3, m, n, k)
+            log(f"[dit {m}x{n}x{k}] {json.dumps(out[f'dit_{m}x{n}x{k}'])}")
     if "blr" in only:
         out["blr"] = bench_blr(torch, bw, max(K // 10, 20), max(W // 5, 5))
         log(f"[blr] {json.dumps(out['blr'])}")
@@ -411,6 +430,12 @@ def main():
                      "us_per_call": round(v["step_ms"] * 1e3, 3),
                      "us_per_call_min": round(v["step_ms_min"] * 1e3, 3),
                      "hbm_frac": round(v["gbs_step"] / HBM_PEAK_GBS, 4)}
+    for key in [k for k in out if k.startswith("dit_")]:
+        v = out[key]
+        line[key] = {"workload": f"tq2_gemm {key[4:]} (M x N x K, MFMA path, DiT benchmark shape)",
+                     "tflops": round(v["tflops_step"], 2), "us_per_call": round(v["step_ms"] * 1e3, 2),
+                     "us_per_call_min": round(v["step_ms_min"] * 1e3, 2),
+                     "mfma_frac": round(v["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4)}
     if "blr" in out:
         b = out["blr"]
         line["blr"] = {"workload": "blr_forward M=512, d_in=d_out=4096, r=1024 (3 launches per call)",

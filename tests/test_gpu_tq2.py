@@ -137,6 +137,19 @@ def test_prefill_sampled(torch, path):
     check_tq2_sampled(aos, 4096, 4096, x, path, "prefill M=2048", count=4096)
 
 
+DIT_SHAPES = list(wl.DIT_SHAPES)
+
+
+@pytest.mark.parametrize("path", ["f32", "mfma"])
+@pytest.mark.parametrize("m,n,k", DIT_SHAPES)
+def test_dit_shapes_sampled(torch, m, n, k, path):
+    """The DiT benchmark shapes of "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs" (LCG
+    weights, scale 0.0625): K = 3072 is 24 blocks, and 1536 x 3072 gives fewer 128 x 256
+    tiles than the chip has CUs."""
+    aos, x = wl.dit_weight(n, k), wl.dit_x(m, k)
+    check_tq2_sampled(aos, n, k, x, path, f"DiT {m}x{n}x{k}", count=4096)
+
+
 def test_results_are_deterministic(torch):
     aos, x = wl.mlp_inputs(32)
     w = bw.tq2_upload(aos, 14336, 4096)

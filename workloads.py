@@ -154,6 +154,9 @@ def sweep_x(m: int, k: int) -> np.ndarray:
     return (np.sin(t).astype(np.float32) + row * np.float32(0.0005)).astype(np.float32)
 
 
+DIT_SHAPES = ((1536, 27648, 3072), (1536, 3072, 3072))  # (M, N, K) of the page's DiT benchmarks
+
+
 def dit_weight(n: int, k: int):
     """Weight of the page's DiT benchmarks: LCG seed 0xDEADBEEF ^ N, scale 0.0625."""
     codes = lcg_codes((0xDEADBEEF ^ n) & 0xFFFFFFFF, n * k).reshape(n, k)
