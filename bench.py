@@ -15,7 +15,7 @@ the timed region holds GPU work only (host launch cost removed); HIP events on
 the launch stream bracket the replay.  Each step is one library call.  The same
 K steps issued eagerly from Python are also timed and reported as context.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mlp,dit,blr,cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mlp,dit,blr,dense,cpu]
 """
 
 from __future__ import annotations
@@ -212,6 +212,40 @@ def bench_blr(torch, bw, steps, warmup):
     return t
 
 
+def dense_baseline(torch, bw, steps, m, n, k, aos, x_np, reps=5):
+    """The unfused alternative: decode the weight to dense f32 (tq2_dequant), cast it to
+    f16, multiply with torch.matmul (the vendor GEMM, called as a library), cast y back to
+    f32.  Timed eagerly (no graph capture of the library GEMM), median of `reps` runs of
+    `steps` calls; the weight and activations are resident in HBM."""
+    w = bw.tq2_upload(aos, n, k)
+    x = torch.from_numpy(x_np).cuda()
+    wf = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    w16 = torch.empty((n, k), dtype=torch.float16, device="cuda")
+    x16 = torch.empty((m, k), dtype=torch.float16, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+    def step():
+        bw.tq2_dequant(w, wf)
+        w16.copy_(wf)
+        x16.copy_(x)
+        y.copy_(torch.matmul(x16, w16.t()))
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / steps)
+    w.close()
+    return float(np.median(times))
+
+
 def context_floors(torch, steps=500):
     """What the box itself allows, measured the same way as the workloads: the
     per-launch cost of a one-element fill kernel in a replayed graph, and the
@@ -337,7 +371,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--only", default="decode,prefill,mlp,dit,blr,cpu")
+    ap.add_argument("--only", default="decode,prefill,mlp,dit,blr,dense,cpu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
@@ -444,6 +478,20 @@ def main():
                        "mfma_frac": round(b["tflops_step"] / MFMA_F16_PEAK_TFLOPS, 4)}
     if "decode" in only:
         line["context"] = context_floors(torch)
+    if "dense" in only:
+        try:
+            aos, x_np = wl.decode_inputs()
+            dec = dense_baseline(torch, bw, 200, 1, wl.DECODE["N"], wl.DECODE["K"], aos, x_np)
+            aos, x_np = wl.prefill_inputs()
+            pm, pn, pk = wl.PREFILL["M"], wl.PREFILL["N"], wl.PREFILL["K"]
+            pre = dense_baseline(torch, bw, 20, pm, pn, pk, aos, x_np)
+            line["dense_dequant_baseline"] = {
+                "decode_us_per_call": round(dec * 1e3, 2), "prefill_us_per_call": round(pre * 1e3, 2),
+                "prefill_tflops": round(2.0 * pm * pn * pk / (pre * 1e-3) / 1e12, 2),
+                "what": "tq2_dequant to dense f32, cast to f16, torch.matmul f16 (vendor GEMM), y cast to "
+                        "f32; eager, weight resident; the unfused alternative to tq2_gemm"}
+        except Exception as e:  # a baseline only: report, do not fail the bench line
+            line["dense_dequant_baseline"] = {"error": repr(e)[:200]}
     if "cpu" in only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
