@@ -6,7 +6,7 @@ There is no CPU fallback: if the library is missing or fails to load, the calls
 raise.
 
 Names follow the C ABI in include/libtq2.h: tq2_upload, tq2_free, tq2_gemm,
-tq2_gemm_path, tq2_dequant, blr_forward, blr_workspace_size, tq2_select_path,
+tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_workspace_size, tq2_select_path,
 tq2_set_m_small, tq2_strerror, tq2_version.
 """
 
@@ -67,6 +67,7 @@ def lib():
         "tq2_dequant": ([p, p, p], i32),
         "blr_workspace_size": ([i64, i64, i64, i64], sz),
         "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "blr_forward_paths": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
         "tq2_strerror": ([i32], ctypes.c_char_p),
         "tq2_version": ([], ctypes.c_char_p),
     }
@@ -219,4 +220,29 @@ def blr_forward(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None)
                              _dev(y, torch.float32, "y"), m, d_in, d_out, r,
                              _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
            "blr_forward")
+    return y
+
+
+def blr_forward_paths(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
+    """A layer of P paths, y = sum_p h_p . c_p, rounded path by path; the per-path
+    operands are stacked along a leading P axis (bits_u [P][d_out][r/32], bits_v
+    [P][d_in][r/32], h [P][d_out], l [P][r], g [P][d_in])."""
+    import torch
+
+    m, d_in = x.shape
+    npaths, d_out = h.shape
+    r = l.shape[1]
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
+    need = blr_workspace_size(m, d_in, d_out, r)
+    if need == 0:
+        raise Tq2Error(TQ2_EINVAL, "blr_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().blr_forward_paths(npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
+                                   _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
+                                   _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
+                                   _dev(y, torch.float32, "y"), m, d_in, d_out, r,
+                                   _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+           "blr_forward_paths")
     return y

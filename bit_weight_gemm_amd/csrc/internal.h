@@ -59,8 +59,9 @@ struct BlrPlan {
     size_t off_codes_v, off_codes_u, off_al, off_xg, total;
 };
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+// accumulate: y = f32(y + f32(h*c)) instead of y = f32(h*c) (later paths of a layer)
 hipError_t launch_blr_forward(const BlrPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
-                              void *workspace, hipStream_t s);
+                              void *workspace, bool accumulate, hipStream_t s);
 
 }  // namespace tq2

@@ -262,30 +262,51 @@ size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     return tq2::blr_plan(M, d_in, d_out, r).total;
 }
 
-int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
-                const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *workspace,
-                size_t workspace_bytes, void *stream) {
+// Host-side checks shared by the BLR entry points: P stacked paths of the given
+// sizes (P = 1 for blr_forward).  Returns TQ2_OK or the status to report.
+static int blr_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                     const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                     void *workspace, size_t workspace_bytes) {
     const size_t need = blr_workspace_size(M, d_in, d_out, r);
-    if (need == 0) return TQ2_EINVAL;
-    int dev = -1;
-    int st = check_device(&dev);
-    if (st) return st;
-    if (M == 0) return TQ2_OK;
+    if (need == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
     if (!bits_u || !bits_v || !h || !l || !g || !x || !y || !workspace) return TQ2_EINVAL;
     if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TQ2_EINVAL;
     if (!aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(bits_u) & 3u) ||
         (reinterpret_cast<uintptr_t>(bits_v) & 3u) || (reinterpret_cast<uintptr_t>(h) & 3u) ||
         (reinterpret_cast<uintptr_t>(l) & 3u) || (reinterpret_cast<uintptr_t>(g) & 3u))
         return TQ2_EINVAL;
-    const size_t ybytes = (size_t)M * d_out * 4;
+    const size_t ybytes = (size_t)M * d_out * 4, p = (size_t)P;
     if (overlap(y, ybytes, x, (size_t)M * d_in * 4) || overlap(y, ybytes, workspace, need) ||
-        overlap(y, ybytes, bits_u, (size_t)d_out * (r / 32) * 4) ||
-        overlap(y, ybytes, bits_v, (size_t)d_in * (r / 32) * 4) || overlap(y, ybytes, h, (size_t)d_out * 4) ||
-        overlap(y, ybytes, l, (size_t)r * 4) || overlap(y, ybytes, g, (size_t)d_in * 4))
+        overlap(y, ybytes, bits_u, p * d_out * (r / 32) * 4) || overlap(y, ybytes, bits_v, p * d_in * (r / 32) * 4) ||
+        overlap(y, ybytes, h, p * d_out * 4) || overlap(y, ybytes, l, p * r * 4) || overlap(y, ybytes, g, p * d_in * 4))
         return TQ2_EINVAL;
+    return TQ2_OK;
+}
+
+int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return blr_forward_paths(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace, workspace_bytes, stream);
+}
+
+int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                      const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (blr_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
+    int dev = -1;
+    int st = check_device(&dev);
+    if (st) return st;
+    if (M == 0) return TQ2_OK;
+    st = blr_check(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace, workspace_bytes);
+    if (st) return st;
     const tq2::BlrPlan plan = tq2::blr_plan(M, d_in, d_out, r);
-    return from_hip(tq2::launch_blr_forward(plan, bits_u, bits_v, h, l, g, x, y, workspace,
-                                            static_cast<hipStream_t>(stream)));
+    const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
+    for (int64_t p = 0; p < P; ++p) {
+        st = from_hip(tq2::launch_blr_forward(plan, bits_u + p * wu, bits_v + p * wv, h + p * d_out, l + p * r,
+                                              g + p * d_in, x, y, workspace, p > 0, static_cast<hipStream_t>(stream)));
+        if (st) return st;
+    }
+    return TQ2_OK;
 }
 
 }  // extern "C"

@@ -32,8 +32,9 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // Epilogues: plain f32 store; f32 store times a factor per output column;
 // f16 store (round to nearest even) of the product with a factor per column,
-// 0 past the first nrowf columns.
-enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2 };
+// 0 past the first nrowf columns; f32 accumulate of the rounded product with a
+// factor per column, C = f32(C + f32(f*v)) (no fused multiply-add).
+enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3 };
 
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
             if (gn >= p.N) continue;
             float rf = 1.0f;
-            if constexpr (EPI == kEpiRowScale) rf = p.rowf[gn];
+            if constexpr (EPI == kEpiRowScale || EPI == kEpiRowScaleAcc) rf = p.rowf[gn];
             if constexpr (EPI == kEpiHalfScale) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
             float *C = p.C + blockIdx.y * p.c_slice;
 #pragma unroll
@@ -382,9 +383,15 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (gm < p.M) {
                     const float v = acc[mb][nb][r];
-                    if constexpr (EPI == kEpiHalfScale)
+                    if constexpr (EPI == kEpiHalfScale) {
                         p.Ch[(int64_t)gm * p.ldc + gn] = (_Float16)(rf * v);
-                    else
+                    } else if constexpr (EPI == kEpiRowScaleAcc) {
+                        // two roundings: the product must not be fused into the sum
+#pragma clang fp contract(off)
+                        float *c = C + (int64_t)gm * p.ldc + gn;
+                        const float prod = rf * v;
+                        *c = *c + prod;
+                    } else
                         C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
                 }
             }
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
 
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
-                              void *workspace, hipStream_t s) {
+                              void *workspace, bool accumulate, hipStream_t s) {
     char *ws = static_cast<char *>(workspace);
     uint32_t *codes_v = reinterpret_cast<uint32_t *>(ws + pl.off_codes_v);
     uint32_t *codes_u = reinterpret_cast<uint32_t *>(ws + pl.off_codes_u);
@@ -623,14 +630,16 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
         e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiHalfScale>(p1, s);
     }
     if (e != hipSuccess) return e;
-    // GEMM2: y[M][d_out] = h . (al . S_U^T)
+    // GEMM2: c = al . S_U^T, written as y (see below)
     GemmArgs p2{};
     p2.Ah = al, p2.lda = pl.kpad2, p2.colf = nullptr;
     p2.codes = codes_u, p2.kw = pl.kpad2 / 16, p2.scales = nullptr, p2.kbw = 0;
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
     p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.kpad2, p2.Kloop = (int)pl.kpad2;
     p2.a_vec = 1;
-    return run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScale, 2, 1>(p2, s);
+    // y = h . c (later paths of a layer: y = f32(y + f32(h . c)))
+    return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScaleAcc, 2, 1>(p2, s)
+                      : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScale, 2, 1>(p2, s);
 }
 
 }  // namespace tq2

@@ -26,7 +26,9 @@
  *         binary low-rank layer W^ = diag(h) S_U diag(l) S_V^T diag(g) and its
  *         forward a = (x.g) S_V, c = (a.l) S_U^T, y = h.c; `expand` fixes the sign
  *         bitmap (bit j of word w is rank index 32w+j, set = +1, clear = -1);
- *         `blr_forward` overwrites y and stages x.g and a.l in f16.
+ *         `blr_forward` overwrites y and stages x.g and a.l in f16; a layer is
+ *         the sum of its paths (y = sum_p W^_p x), two paths combined by
+ *         `scale_acc2` as fl(fl(h_0 c_0) + fl(h_1 c_1)).
  */
 #ifndef LIBTQ2_H
 #define LIBTQ2_H
@@ -113,6 +115,20 @@ size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                 const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
                 int64_t r, void *workspace, size_t workspace_bytes, void *stream);
+
+/* [BLR] A layer of P paths, y = sum_p h_p . c_p, each path the product of
+ * blr_forward with its own bitmaps and vectors (all paths share M, d_in, d_out
+ * and r).  The sum is rounded path by path as the page's scale_acc /
+ * scale_acc2 kernels round it: y = f32(h_0*c_0), then y = f32(y + f32(h_p*c_p))
+ * for p = 1 .. P-1, each product rounded before the addition.  Per-path operands
+ * are stacked in device memory: bits_u [P][d_out][r/32], bits_v [P][d_in][r/32],
+ * h [P][d_out], l [P][r], g [P][d_in].  Requires P >= 1 and everything
+ * blr_forward requires; the workspace is one path's (blr_workspace_size),
+ * reused by the paths in turn, so the paths run one after another on `stream`.
+ * P == 1 gives blr_forward's result. */
+int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                      const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *tq2_strerror(int status);

@@ -145,3 +145,24 @@ def blr_bound_at(bits_u, bits_v, h, l, g, x, ti, ii) -> np.ndarray:
     _check(lib().blr_oracle_bound_at(_ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l), _ptr(g), _ptr(x),
                                      m, d_in, h.size, l.size, _ptr(ti), _ptr(ii), ti.size, _ptr(b)))
     return b
+
+
+def blr_forward_paths(paths, x) -> np.ndarray:
+    """y64 of a layer of several paths: the sum over paths, in path order, of each
+    path's forward ("cortiq-engine 0.8.43 -- train_mm.rs": a Blr layer is y = sum_p
+    W^_p x; the f64 reference of its two-path layer test adds h_p c_p path by path).
+    `paths` is a sequence of dicts with bits_u, bits_v, h, l, g."""
+    y = None
+    for p in paths:
+        yp, _ = blr_forward(p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"], x)
+        y = yp if y is None else y + yp
+    return y
+
+
+def blr_paths_bound_at(paths, x, ti, ii) -> np.ndarray:
+    """Sum over paths of each path's dense-equivalent bound at outputs (ti, ii)."""
+    b = None
+    for p in paths:
+        bp = blr_bound_at(p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"], x, ti, ii)
+        b = bp if b is None else b + bp
+    return b

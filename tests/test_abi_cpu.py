@@ -38,7 +38,7 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for must in ("tq2_upload", "tq2_free", "tq2_gemm", "tq2_gemm_path", "tq2_dequant", "blr_forward",
-                 "blr_workspace_size", "tq2_select_path", "tq2_set_m_small", "tq2_strerror", "tq2_version",
+                 "blr_forward_paths", "blr_workspace_size", "tq2_select_path", "tq2_set_m_small", "tq2_strerror", "tq2_version",
                  "tq2_weight_info"):
         assert must in names, must
 
@@ -95,3 +95,6 @@ def test_auto_path_threshold(L):
 def test_blr_forward_rejects_bad_sizes_on_the_host(L):
     # r % 32 != 0 is refused before any pointer or device is looked at
     assert L.blr_forward(None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
+    # a layer needs at least one path; bad sizes are refused as for one path
+    assert L.blr_forward_paths(0, None, None, None, None, None, None, None, 4, 8, 8, 32, None, 0, None) == bw.TQ2_EINVAL
+    assert L.blr_forward_paths(2, None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL

@@ -144,3 +144,71 @@ def test_blr_deterministic(torch):
     d = wl.blr_inputs(m=100, d_in=512, d_out=384, r=256, index=2)
     a, b = _run(d), _run(d)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _stack(paths, key):
+    return np.ascontiguousarray(np.stack([p[key] for p in paths]))
+
+
+def _run_paths(paths, x):
+    torch = torch_cuda()
+    m, d_out = x.shape[0], paths[0]["h"].size
+    base = torch.full((m * d_out + 64,), float("nan"), device="cuda")
+    y = base[: m * d_out].view(m, d_out)
+    bw.blr_forward_paths(bits_dev(_stack(paths, "bits_u")), bits_dev(_stack(paths, "bits_v")),
+                         to_dev(_stack(paths, "h")), to_dev(_stack(paths, "l")), to_dev(_stack(paths, "g")),
+                         to_dev(x), y)
+    torch.cuda.synchronize()
+    assert np.isnan(base[m * d_out:].cpu().numpy()).all(), "write past the end of y"
+    out = y.cpu().numpy()
+    assert not np.isnan(out).any(), "unwritten outputs"
+    return out
+
+
+def _page_paths(n_paths):
+    paths = [wl.blr_page_inputs(path=p) for p in range(n_paths)]
+    x = paths[0].pop("x")
+    for p in paths[1:]:
+        p.pop("x")
+    return paths, x
+
+
+def test_blr_two_path_layer_matches_oracle(torch):
+    """The trainer's two-path layer test ("cortiq-engine 0.8.43 -- train_mm.rs",
+    blr_layer_matches_host: m=256, n=384, r=128, 70 tokens, np=2): relative Frobenius
+    error < 3e-3 against the f64 sum of the paths, and every output within 4e-3 of the
+    summed dense-equivalent bounds."""
+    paths, x = _page_paths(2)
+    note("[blr paths] two-path trainer layer")
+    y = _run_paths(paths, x)
+    y64 = oracle.blr_forward_paths(paths, x)
+    e = _rel_frob(y, y64)
+    note(f"  two paths: relative Frobenius error {e:.3g}")
+    assert e < 3e-3
+    ti = np.repeat(np.arange(x.shape[0]), y.shape[1])
+    ii = np.tile(np.arange(y.shape[1]), x.shape[0])
+    b = oracle.blr_paths_bound_at(paths, x, ti, ii)
+    assert_within(y[ti, ii], y64[ti, ii], b, MFMA_REL, "two-path layer")
+
+
+@pytest.mark.parametrize("n_paths,shape", [(2, None), (3, (70, 45, 130, 96)), (3, (512, 4096, 512, 1024))])
+def test_blr_paths_round_path_by_path(torch, n_paths, shape):
+    """The layer output is the single-path outputs added in f32, path by path, to the
+    bit: y = f32(f32(h_0 c_0) + f32(h_1 c_1)) (scale_acc2), then + f32(h_2 c_2)."""
+    if shape is None:
+        paths, x = _page_paths(n_paths)
+    else:
+        m, d_in, d_out, r = shape
+        paths = [wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=30 + p) for p in range(n_paths)]
+        x = paths[0]["x"]
+        for p in paths:
+            p.pop("x")
+    note(f"[blr paths] {n_paths} paths, M={x.shape[0]} d_in={x.shape[1]}")
+    y = _run_paths(paths, x)
+    want = None
+    for p in paths:
+        yp = _run(dict(p, x=x))
+        want = yp if want is None else (want + yp).astype(np.float32)
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+    one = _run_paths(paths[:1], x)
+    assert np.array_equal(one.view(np.uint32), _run(dict(paths[0], x=x)).view(np.uint32))

@@ -377,3 +377,42 @@ def test_blr_rejects_bad_arguments():
     d = wl.blr_inputs(m=2, d_in=8, d_out=8, r=32, index=1)
     with pytest.raises(oracle.OracleError):
         oracle.blr_bound_at(**d, ti=[2], ii=[0])   # token index out of range
+
+
+def test_blr_paths_cancel_and_add_exactly():
+    """A layer is the sum of its paths: a second path equal to the first but with every
+    S_U sign flipped gives c_1 = -c_0 exactly, so the layer output is exactly zero;
+    two equal paths give exactly twice one path (scaling by 2 is exact in f64)."""
+    d = wl.blr_inputs(m=5, d_in=40, d_out=24, r=64, index=11)
+    x = d.pop("x")
+    flipped = dict(d, bits_u=~d["bits_u"])
+    assert np.all(oracle.blr_forward_paths([d, flipped], x) == 0.0)
+    one, _ = oracle.blr_forward(**d, x=x)
+    assert np.array_equal(oracle.blr_forward_paths([d, d], x), 2.0 * one)
+    assert np.array_equal(oracle.blr_forward_paths([d], x), one)
+
+
+def test_blr_paths_dense_equivalence_exact():
+    """Two different paths against y = x (W^_0 + W^_1)^T in exact rationals: each path
+    within its own f64 error bound (as for one path), plus one rounding of the sum."""
+    m, d_in, d_out, r = 2, 24, 16, 32
+    paths = [wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=12 + p) for p in range(2)]
+    x = paths[0]["x"]
+    for d in paths:
+        d["x"] = x
+    y = oracle.blr_forward_paths(paths, x)
+    F = lambda v: Fraction(float(v))
+    W = [[Fraction(0)] * d_in for _ in range(d_out)]
+    tri = np.zeros((m, d_out))
+    for d in paths:
+        su, sv = _np_signs(d["bits_u"], r), _np_signs(d["bits_v"], r)
+        l = [F(v) for v in d["l"]]
+        for i in range(d_out):
+            for j in range(d_in):
+                W[i][j] += F(d["h"][i]) * F(d["g"][j]) * sum((int(su[i, k]) * l[k] * int(sv[j, k]) for k in range(r)), Fraction(0))
+        tri += _triple_abs(d)
+    for t in range(m):
+        for i in range(d_out):
+            exact = sum((F(x[t, j]) * W[i][j] for j in range(d_in)), Fraction(0))
+            err = abs(Fraction(y[t, i]) - exact)
+            assert err <= Fraction((d_in + r + 3) * U53 * tri[t, i]) + Fraction(U53) * abs(Fraction(y[t, i])), (t, i)
