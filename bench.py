@@ -278,6 +278,25 @@ def context_floors(torch, steps=500):
                     "copy: 256 MiB device copy, bytes read + written"}
 
 
+def bench_blr_backward(torch, bw, steps, warmup):
+    """Backward of the BLR workload (one path), dy ~ 1e-3 N(0, 1), gradient scale 1024."""
+    d = wl.blr_inputs()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    m, d_in = d["x"].shape
+    d_out, r = d["h"].size, d["l"].size
+    bu, bv = dev(d["bits_u"].view(np.int32)[None]), dev(d["bits_v"].view(np.int32)[None])
+    h, l, g, x = dev(d["h"][None]), dev(d["l"][None]), dev(d["g"][None]), dev(d["x"])
+    dy = dev((np.random.default_rng(4).standard_normal((m, d_out)) * 1e-3).astype(np.float32))
+    dh, dl, dg = (torch.zeros((1, n), device="cuda") for n in (d_out, r, d_in))
+    dx = torch.empty((m, d_in), device="cuda")
+    ws = torch.empty(bw.blr_backward_workspace_size(m, d_in, d_out, r), dtype=torch.uint8, device="cuda")
+    t = Timer(torch).run(lambda i: bw.blr_backward_paths(bu, bv, h, l, g, x, dy, dh, dl, dg, dx=dx, workspace=ws),
+                         steps, warmup)
+    flop = 2.0 * m * r * (d_in + d_out)  # the two gradient products; a and c are recomputed on top
+    t.update(flop_per_call=flop, tflops_step=flop / (t["step_ms"] * 1e-3) / 1e12)
+    return t
+
+
 def calib_copy(torch, reps=5):
     """Untimed device copies of known size, for scaling the HBM byte counters."""
     a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -422,6 +441,8 @@ def main():
     if "blr" in only:
         out["blr"] = bench_blr(torch, bw, max(K // 10, 20), max(W // 5, 5))
         log(f"[blr] {json.dumps(out['blr'])}")
+        out["blr_backward"] = bench_blr_backward(torch, bw, max(K // 20, 20), max(W // 5, 5))
+        log(f"[blr] {json.dumps(out['blr'])}")
 
     line = {
         "metric": "TQ2 GEMM weight-GB/s (M=1) and TFLOP/s (M=2048), % of HBM/MFMA roofline",
@@ -492,6 +513,12 @@ def main():
                         "f32; eager, weight resident; the unfused alternative to tq2_gemm"}
         except Exception as e:  # a baseline only: report, do not fail the bench line
             line["dense_dequant_baseline"] = {"error": repr(e)[:200]}
+    if "blr_backward" in out:
+        b = out["blr_backward"]
+        line["blr_backward"] = {"workload": "blr_backward_paths, one path, M=512, d_in=d_out=4096, r=1024 "
+                                            "(a and c recomputed; 12 launches per call)",
+                                "tflops_algorithmic": round(b["tflops_step"], 2),
+                                "ms_per_call": b["step_ms"], "ms_per_call_min": b["step_ms_min"]}
     if "cpu" in only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

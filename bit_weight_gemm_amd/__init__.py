@@ -6,7 +6,8 @@ There is no CPU fallback: if the library is missing or fails to load, the calls
 raise.
 
 Names follow the C ABI in include/libtq2.h: tq2_upload, tq2_free, tq2_gemm,
-tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_workspace_size, tq2_select_path,
+tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_backward_paths,
+blr_workspace_size, blr_backward_workspace_size, tq2_select_path,
 tq2_set_m_small, tq2_strerror, tq2_version.
 """
 
@@ -68,6 +69,9 @@ def lib():
         "blr_workspace_size": ([i64, i64, i64, i64], sz),
         "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
         "blr_forward_paths": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "blr_backward_workspace_size": ([i64, i64, i64, i64], sz),
+        "blr_backward_paths": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
+        "blr_backward": ([p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
         "tq2_strerror": ([i32], ctypes.c_char_p),
         "tq2_version": ([], ctypes.c_char_p),
     }
@@ -246,3 +250,34 @@ def blr_forward_paths(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream
                                    _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
            "blr_forward_paths")
     return y
+
+
+def blr_backward_workspace_size(m: int, d_in: int, d_out: int, r: int) -> int:
+    return int(lib().blr_backward_workspace_size(m, d_in, d_out, r))
+
+
+def blr_backward_paths(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx=None, gscale=1024.0, workspace=None,
+                       stream=None):
+    """Backward of blr_forward_paths on the same x: dh [P][d_out], dl [P][r] and dg [P][d_in]
+    are accumulated in place; dx [M][d_in] is overwritten (returned)."""
+    import torch
+
+    m, d_in = x.shape
+    npaths, d_out = h.shape
+    r = l.shape[1]
+    if dx is None:
+        dx = torch.empty((m, d_in), dtype=torch.float32, device=x.device)
+    need = blr_backward_workspace_size(m, d_in, d_out, r)
+    if need == 0:
+        raise Tq2Error(TQ2_EINVAL, "blr_backward_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().blr_backward_paths(npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
+                                    _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
+                                    _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
+                                    _dev(dy, torch.float32, "dy"), _dev(dx, torch.float32, "dx"),
+                                    _dev(dh, torch.float32, "dh"), _dev(dl, torch.float32, "dl"),
+                                    _dev(dg, torch.float32, "dg"), m, d_in, d_out, r, float(gscale),
+                                    _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+           "blr_backward_paths")
+    return dx

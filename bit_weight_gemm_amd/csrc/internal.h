@@ -59,6 +59,20 @@ struct BlrPlan {
     size_t off_codes_v, off_codes_u, off_al, off_xg, total;
 };
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+// Binary low-rank backward: the forward's carve-up, then the backward's buffers.
+struct BlrBwdPlan {
+    BlrPlan fwd;
+    int64_t kpado;               // d_out padded: contraction length of db = (dy.h) S_U
+    int64_t npadi;               // d_in padded: rows of S_V as the B operand of dx'
+    int64_t chunks;              // token chunks of the column sums
+    size_t off_codes_ut, off_codes_vt, off_a, off_c, off_dyh, off_db, off_dbl, off_dxp, off_part, total;
+};
+BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+// dh, dl, dg accumulate; dx is overwritten (accumulate_dx: dx = f32(dx + f32(g.dx')))
+hipError_t launch_blr_backward(const BlrBwdPlan &p, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                               const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                               float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s);
+
 // accumulate: y = f32(y + f32(h*c)) instead of y = f32(h*c) (later paths of a layer)
 hipError_t launch_blr_forward(const BlrPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,

@@ -309,4 +309,61 @@ int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v,
     return TQ2_OK;
 }
 
+size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    if (blr_workspace_size(M, d_in, d_out, r) == 0) return 0;
+    return tq2::blr_bwd_plan(M, d_in, d_out, r).total;
+}
+
+int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                       const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    const size_t need = blr_backward_workspace_size(M, d_in, d_out, r);
+    if (need == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 64) return TQ2_EINVAL;  // token chunks fit grid.y
+    int e2 = 0;
+    if (!std::isfinite(gscale) || gscale <= 0.0f || std::frexp(gscale, &e2) != 0.5f || gscale > 65536.0f)
+        return TQ2_EINVAL;  // a power of two, at most 2^16
+    int dev = -1;
+    int st = check_device(&dev);
+    if (st) return st;
+    if (!bits_u || !bits_v || !h || !l || !g || !x || !dy || !dx || !dh || !dl || !dg || !workspace) return TQ2_EINVAL;
+    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TQ2_EINVAL;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(bits_u) | reinterpret_cast<uintptr_t>(bits_v) |
+                          reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(g) |
+                          reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
+                          reinterpret_cast<uintptr_t>(dx) | reinterpret_cast<uintptr_t>(dh) |
+                          reinterpret_cast<uintptr_t>(dl) | reinterpret_cast<uintptr_t>(dg);
+    if ((mis & 3u) || (reinterpret_cast<uintptr_t>(l) & 15u)) return TQ2_EINVAL;
+    const size_t p = (size_t)P;
+    struct Span { const void *ptr; size_t bytes; };
+    const Span outs[] = {{dx, (size_t)M * d_in * 4}, {dh, p * d_out * 4}, {dl, p * r * 4}, {dg, p * d_in * 4}};
+    const Span ins[] = {{bits_u, p * d_out * (r / 32) * 4}, {bits_v, p * d_in * (r / 32) * 4}, {h, p * d_out * 4},
+                        {l, p * r * 4}, {g, p * d_in * 4}, {x, (size_t)M * d_in * 4}, {dy, (size_t)M * d_out * 4},
+                        {workspace, need}};
+    for (size_t i = 0; i < 4; ++i) {
+        for (const Span &in : ins)
+            if (outs[i].bytes && in.bytes && overlap(outs[i].ptr, outs[i].bytes, in.ptr, in.bytes)) return TQ2_EINVAL;
+        for (size_t j = i + 1; j < 4; ++j)
+            if (outs[i].bytes && outs[j].bytes && overlap(outs[i].ptr, outs[i].bytes, outs[j].ptr, outs[j].bytes))
+                return TQ2_EINVAL;
+    }
+    if (M == 0) return TQ2_OK;  // no tokens: no gradient to add, dx is empty
+    const tq2::BlrBwdPlan plan = tq2::blr_bwd_plan(M, d_in, d_out, r);
+    const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
+    for (int64_t q = 0; q < P; ++q) {
+        st = from_hip(tq2::launch_blr_backward(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out, l + q * r,
+                                               g + q * d_in, x, dy, dx, dh + q * d_out, dl + q * r, dg + q * d_in,
+                                               gscale, workspace, q > 0, static_cast<hipStream_t>(stream)));
+        if (st) return st;
+    }
+    return TQ2_OK;
+}
+
+int blr_backward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                 const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M, int64_t d_in,
+                 int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes, void *stream) {
+    return blr_backward_paths(1, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale,
+                              workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

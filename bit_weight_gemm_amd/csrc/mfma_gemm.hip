@@ -33,8 +33,9 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // Epilogues: plain f32 store; f32 store times a factor per output column;
 // f16 store (round to nearest even) of the product with a factor per column,
 // 0 past the first nrowf columns; f32 accumulate of the rounded product with a
-// factor per column, C = f32(C + f32(f*v)) (no fused multiply-add).
-enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3 };
+// factor per column, C = f32(C + f32(f*v)) (no fused multiply-add); f32 store
+// times one scalar factor alpha.
+enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4 };
 
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
@@ -50,6 +51,7 @@ struct GemmArgs {
     int64_t ldc;
     const float *rowf;       // [N] output factor (kEpiRowScale, kEpiHalfScale)
     int nrowf;               // factors present (kEpiHalfScale: columns past it get 0)
+    float alpha;             // output factor (kEpiScale)
     int M, N, K;             // true sizes; K bounds the A loads
     int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
@@ -377,6 +379,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             float rf = 1.0f;
             if constexpr (EPI == kEpiRowScale || EPI == kEpiRowScaleAcc) rf = p.rowf[gn];
             if constexpr (EPI == kEpiHalfScale) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
+            if constexpr (EPI == kEpiScale) rf = p.alpha;
             float *C = p.C + blockIdx.y * p.c_slice;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                         const float prod = rf * v;
                         *c = *c + prod;
                     } else
-                        C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale) ? rf * v : v;
+                        C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale || EPI == kEpiScale) ? rf * v : v;
                 }
             }
         }
@@ -640,6 +643,233 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     // y = h . c (later paths of a layer: y = f32(y + f32(h . c)))
     return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScaleAcc, 2, 1>(p2, s)
                       : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScale, 2, 1>(p2, s);
+}
+
+// ------------------------------------------------------------------ binary low-rank backward
+//
+// "cortiq-engine 0.8.43 -- train_mm.rs", module header: for a path with
+// a = (x.g) S_V and c = (a.l) S_U^T,
+//   dh = sum_t dy.c      db = (dy.h) S_U      dl = sum_t a.db
+//   dx' = (db.l) S_V^T   dg = sum_t x.dx'     dx += g.dx'
+// with the GEMM inputs staged in f16 under a power-of-two gradient scale gs
+// that the GEMM's output factor 1/gs removes again.  a and c are recomputed with
+// the forward's kernels (same tiles, so the same values as the forward's).
+// The two new products read the bitmaps in the other orientation: S_U^T (rows
+// r, contraction d_out) is laid out as S_V is for the forward, and S_V (rows d_in,
+// contraction r) as S_U is.  Column sums over the tokens go in two passes, chunks
+// of kColChunk tokens then the chunks in order, so results do not depend on timing.
+
+constexpr int kColChunk = 64;
+
+BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    BlrBwdPlan p{};
+    p.fwd = blr_plan(M, d_in, d_out, r);
+    p.kpado = round_up(d_out, kBlrKPad);
+    p.npadi = round_up(d_in, kRowPad);
+    p.chunks = (M + kColChunk - 1) / kColChunk;
+    const int64_t widest = d_in > d_out ? (d_in > r ? d_in : r) : (d_out > r ? d_out : r);
+    size_t off = p.fwd.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return at;
+    };
+    p.off_codes_ut = take((size_t)p.fwd.npad1 * (p.kpado / 16) * 4);
+    p.off_codes_vt = take((size_t)p.npadi * (p.fwd.kpad2 / 16) * 4);
+    p.off_a = take((size_t)M * r * 4);
+    p.off_c = take((size_t)M * d_out * 4);
+    p.off_dyh = take((size_t)M * p.kpado * 2);
+    p.off_db = take((size_t)M * r * 4);
+    p.off_dbl = take((size_t)M * p.fwd.kpad2 * 2);
+    p.off_dxp = take((size_t)M * d_in * 4);
+    p.off_part = take((size_t)(p.chunks > 0 ? p.chunks : 1) * widest * 4);
+    p.total = off;
+    return p;
+}
+
+namespace {
+
+enum ColMode { kColStageH = 0, kColDx = 1, kColDxAcc = 2 };
+
+// Pass 1 of a column sum: part[ch][n] = sum over tokens t of chunk ch of
+// A[t][n] * B[t][n] (f32, ascending t), for n < N.  Fused with the elementwise
+// op that reads the same operand A:
+//   kColStageH: H[t][n] = f16(A[t][n] * f[n] * gs) for n < N, 0 for N <= n < ldh;
+//   kColDx:     D[t][n] = f[n] * B[t][n];
+//   kColDxAcc:  D[t][n] = f32(D[t][n] + f32(f[n] * B[t][n])).
+struct ColArgs {
+    const float *A, *B, *f;
+    float *part;
+    _Float16 *H;
+    float *D;
+    int64_t M, N, lda, ldh;
+    float gs;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
+#pragma clang fp contract(off)
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t ch = blockIdx.y;
+    const int64_t t0 = ch * kColChunk, t1 = t0 + kColChunk < q.M ? t0 + kColChunk : q.M;
+    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
+    if (n >= ncols) return;
+    if (n >= q.N) {  // padding columns of the staged operand
+        for (int64_t t = t0; t < t1; ++t) q.H[t * q.ldh + n] = (_Float16)0.0f;
+        return;
+    }
+    const float f = q.f[n];
+    float sum = 0.0f;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float a = q.A[t * q.lda + n], b = q.B[t * q.lda + n];
+        sum = sum + a * b;  // product rounded before the sum (no contraction in this kernel)
+        if constexpr (MODE == kColStageH) q.H[t * q.ldh + n] = (_Float16)(a * f * q.gs);
+        if constexpr (MODE == kColDx) q.D[t * q.lda + n] = f * b;
+        if constexpr (MODE == kColDxAcc) {
+            const float prod = f * b;
+            q.D[t * q.lda + n] = q.D[t * q.lda + n] + prod;
+        }
+    }
+    q.part[ch * q.N + n] = sum;
+}
+
+// Pass 2: out[n] = f32(out[n] + f32(sum over chunks in order of part[ch][n])).
+__global__ __launch_bounds__(256) void blr_colsum_finish_kernel(const float *__restrict__ part, float *__restrict__ out,
+                                                                int64_t N, int64_t chunks) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float s = 0.0f;
+    for (int64_t ch = 0; ch < chunks; ++ch) s += part[ch * N + n];
+    out[n] = out[n] + s;
+}
+
+template <int MODE>
+hipError_t colsum(const ColArgs &q, float *out, int64_t chunks, hipStream_t s) {
+    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
+    blr_colsum_kernel<MODE><<<dim3((unsigned)((ncols + 255) / 256), (unsigned)chunks), dim3(256), 0, s>>>(q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    blr_colsum_finish_kernel<<<dim3((unsigned)((q.N + 255) / 256)), dim3(256), 0, s>>>(q.part, out, q.N, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                               const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                               float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s) {
+    const BlrPlan &pl = pb.fwd;
+    const int64_t M = pl.M, d_in = pl.d_in, d_out = pl.d_out, r = pl.r;
+    char *ws = static_cast<char *>(workspace);
+    auto at = [&](size_t off) { return ws + off; };
+    uint32_t *codes_v = reinterpret_cast<uint32_t *>(at(pl.off_codes_v));
+    uint32_t *codes_u = reinterpret_cast<uint32_t *>(at(pl.off_codes_u));
+    uint32_t *codes_ut = reinterpret_cast<uint32_t *>(at(pb.off_codes_ut));
+    uint32_t *codes_vt = reinterpret_cast<uint32_t *>(at(pb.off_codes_vt));
+    _Float16 *xg = reinterpret_cast<_Float16 *>(at(pl.off_xg));
+    float *a = reinterpret_cast<float *>(at(pb.off_a));
+    float *c = reinterpret_cast<float *>(at(pb.off_c));
+    _Float16 *dyh = reinterpret_cast<_Float16 *>(at(pb.off_dyh));
+    float *db = reinterpret_cast<float *>(at(pb.off_db));
+    _Float16 *dbl = reinterpret_cast<_Float16 *>(at(pb.off_dbl));
+    float *dxp = reinterpret_cast<float *>(at(pb.off_dxp));
+    float *part = reinterpret_cast<float *>(at(pb.off_part));
+    hipError_t e;
+    // bitmaps in both orientations, and f16(x.g)
+    {
+        BlrPrep q{};
+        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
+        q.x = x, q.g = g, q.xg = xg;
+        q.words = r / 32, q.M = M, q.r = r, q.d_in = d_in, q.d_out = d_out;
+        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
+        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
+        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.xvec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+        const int64_t nblk_x = (M * (pl.kpad1 / 8) + 255) / 256;
+        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // S_U^T: rows r, contraction d_out (bits along the rows, as S_V's);
+        // S_V: rows d_in, contraction r (bits along the contraction, as S_U's)
+        BlrPrep t{};
+        t.bits_v = bits_u, t.codes_v = codes_ut, t.d_in = d_out, t.kpad1 = pb.kpado, t.npad1 = pl.npad1;
+        t.bits_u = bits_v, t.codes_u = codes_vt, t.d_out = d_in, t.kpad2 = pl.kpad2, t.npad2 = pb.npadi;
+        t.words = r / 32, t.M = 0, t.r = r;
+        t.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pb.kpado / 16);
+        t.nblk_u = (pb.npadi / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        blr_prep_kernel<<<dim3((unsigned)(t.nblk_v + t.nblk_u)), dim3(256), 0, s>>>(t);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const bool small = blr_small_tiles(M, pl.kpad2);
+    // a = xg . S_V   [M][r]
+    {
+        GemmArgs p{};
+        p.Ah = xg, p.lda = pl.kpad1, p.codes = codes_v, p.kw = pl.kpad1 / 16;
+        p.C = a, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pl.kpad1, p.Kloop = (int)pl.kpad1;
+        if (small)
+            e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiStore>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiStore>(p, s);
+        else
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiStore>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // c = f16(a.l) . S_U^T   [M][d_out]   (a read as f32 and rounded while staged)
+    {
+        GemmArgs p{};
+        p.A = a, p.lda = r, p.colf = l, p.codes = codes_u, p.kw = pl.kpad2 / 16;
+        p.C = c, p.ldc = d_out, p.M = (int)M, p.N = (int)d_out, p.K = (int)r, p.Kloop = (int)pl.kpad2;
+        p.a_vec = 1;
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAVec, true, false, kEpiStore, 2, 1>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dh += sum_t dy.c, with dyh = f16(dy.h.gs) staged from the same reads
+    {
+        ColArgs q{};
+        q.A = dy, q.B = c, q.f = h, q.part = part, q.H = dyh, q.M = M, q.N = d_out, q.lda = d_out, q.ldh = pb.kpado;
+        q.gs = gs;
+        e = colsum<kColStageH>(q, dh, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    // db = dyh . S_U / gs   [M][r]
+    {
+        GemmArgs p{};
+        p.Ah = dyh, p.lda = pb.kpado, p.codes = codes_ut, p.kw = pb.kpado / 16;
+        p.C = db, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
+        p.alpha = 1.0f / gs;
+        if (small)
+            e = (pb.kpado / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiScale>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiScale>(p, s);
+        else
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiScale>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dl += sum_t a.db, with dbl = f16(db.l.gs) staged from the same reads
+    {
+        ColArgs q{};
+        q.A = db, q.B = a, q.f = l, q.part = part, q.H = dbl, q.M = M, q.N = r, q.lda = r, q.ldh = pl.kpad2;
+        q.gs = gs;
+        e = colsum<kColStageH>(q, dl, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    // dx' = dbl . S_V^T / gs   [M][d_in]
+    {
+        GemmArgs p{};
+        p.Ah = dbl, p.lda = pl.kpad2, p.codes = codes_vt, p.kw = pl.kpad2 / 16;
+        p.C = dxp, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
+        p.alpha = 1.0f / gs;
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiScale, 2, 1>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
+    {
+        ColArgs q{};
+        q.A = x, q.B = dxp, q.f = g, q.part = part, q.D = dx, q.M = M, q.N = d_in, q.lda = d_in;
+        e = accumulate_dx ? colsum<kColDxAcc>(q, dg, pb.chunks, s) : colsum<kColDx>(q, dg, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace tq2

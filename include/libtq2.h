@@ -28,7 +28,9 @@
  *         bitmap (bit j of word w is rank index 32w+j, set = +1, clear = -1);
  *         `blr_forward` overwrites y and stages x.g and a.l in f16; a layer is
  *         the sum of its paths (y = sum_p W^_p x), two paths combined by
- *         `scale_acc2` as fl(fl(h_0 c_0) + fl(h_1 c_1)).
+ *         `scale_acc2` as fl(fl(h_0 c_0) + fl(h_1 c_1)); the module header also
+ *         gives the backward (dh, db, dl, dx', dg, dx), and `blr_backward` its f16
+ *         staging under a power-of-two gradient scale.
  */
 #ifndef LIBTQ2_H
 #define LIBTQ2_H
@@ -129,6 +131,34 @@ int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, 
 int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                       const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace blr_backward / blr_backward_paths need (0 on bad sizes). */
+size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/* [BLR] Backward of blr_forward_paths on the same x, path by path (the page's
+ * blr_backward; per path a = (x.g) S_V and c = (a.l) S_U^T as in the forward):
+ *   dh_p += sum_t dy.c      db = (dy.h) S_U      dl_p += sum_t a.db
+ *   dx'  = (db.l) S_V^T     dg_p += sum_t x.dx'  dx = sum_p g.dx'
+ * The two new products stage their inputs in f16 as f16(dy.h.gscale) and
+ * f16(db.l.gscale) and multiply their f32 results by 1/gscale; gscale must be a
+ * power of two in (0, 65536].  a and c are recomputed with the forward's kernels.
+ * Sums over tokens are f32 in a fixed order (chunks of 64 tokens, then the chunks
+ * in order), so results are reproducible.  dh [P][d_out], dl [P][r], dg [P][d_in]
+ * are accumulated (y = f32(y + s)); dx [M][d_in] is overwritten by path 0 and the
+ * later paths add f32(g.dx') to it.  Operands as for blr_forward_paths, plus dy:
+ * device f32 [M][d_out]; all device pointers 4-byte aligned and l 16-byte
+ * aligned; outputs must not overlap each other, the inputs or the workspace.
+ * M <= 4194240 (65535 chunks of 64 tokens); M == 0 is a no-op.
+ * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
+int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                       const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* [BLR] blr_backward_paths with one path. */
+int blr_backward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                 const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M, int64_t d_in,
+                 int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *tq2_strerror(int status);

@@ -166,3 +166,44 @@ def blr_paths_bound_at(paths, x, ti, ii) -> np.ndarray:
         bp = blr_bound_at(p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"], x, ti, ii)
         b = bp if b is None else b + bp
     return b
+
+
+def _signs(bits, r) -> np.ndarray:
+    """[rows][r] of +1.0 / -1.0 from a sign bitmap: rank k is bit k % 32 of word
+    k // 32 of the row, a set bit meaning +1 ("cortiq-engine 0.8.43 -- train_mm.rs",
+    expand)."""
+    bits = np.asarray(bits, dtype=np.uint32)
+    out = np.empty((bits.shape[0], r), dtype=np.float64)
+    for k in range(r):
+        bit = (bits[:, k // 32] >> np.uint32(k % 32)) & np.uint32(1)
+        out[:, k] = np.where(bit == 1, 1.0, -1.0)
+    return out
+
+
+def blr_backward_paths(paths, x, dy):
+    """Backward of a layer of paths, f64 ("cortiq-engine 0.8.43 -- train_mm.rs",
+    module header; the f64 reference of blr_layer_matches_host).  Per path, with
+    a = (x.g) S_V and c = (a.l) S_U^T:
+        dh = sum_t dy.c,  db = (dy.h) S_U,  dl = sum_t a.db,
+        dx' = (db.l) S_V^T,  dg = sum_t x.dx',  and dx = sum_p g.dx'.
+    Returns (dx [M][d_in], [(dh, dl, dg) per path]).  The f16 staging and the
+    gradient scale of the GPU path are not part of the definition."""
+    x64 = np.asarray(x, dtype=np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dx = np.zeros_like(x64)
+    grads = []
+    for p in paths:
+        r = np.asarray(p["l"]).size
+        su = _signs(p["bits_u"], r)   # [d_out][r]
+        sv = _signs(p["bits_v"], r)   # [d_in][r]
+        h, l, g = (np.asarray(p[k], dtype=np.float64) for k in ("h", "l", "g"))
+        a = (x64 * g) @ sv
+        c = (a * l) @ su.T
+        dh = (dy64 * c).sum(axis=0)
+        db = (dy64 * h) @ su
+        dl = (a * db).sum(axis=0)
+        dxp = (db * l) @ sv.T
+        dg = (x64 * dxp).sum(axis=0)
+        dx += g * dxp
+        grads.append((dh, dl, dg))
+    return dx, grads

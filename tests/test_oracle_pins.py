@@ -416,3 +416,41 @@ def test_blr_paths_dense_equivalence_exact():
             exact = sum((F(x[t, j]) * W[i][j] for j in range(d_in)), Fraction(0))
             err = abs(Fraction(y[t, i]) - exact)
             assert err <= Fraction((d_in + r + 3) * U53 * tri[t, i]) + Fraction(U53) * abs(Fraction(y[t, i])), (t, i)
+
+
+def test_blr_backward_euler_identities():
+    """The layer is linear in each of x, h, l and g, so with s = sum dy.y (y from the
+    forward oracle, a separate implementation) the backward must satisfy
+    s = sum x.dx = sum_i h_i dh_i = sum_k l_k dl_k = sum_j g_j dg_j (per path for h, l,
+    g; one path here).  A dropped factor, a transposed sign matrix or a wrong operand in
+    any gradient breaks one of the four."""
+    d = wl.blr_inputs(m=7, d_in=40, d_out=24, r=64, index=13)
+    x = d.pop("x")
+    dy = np.random.default_rng(5).standard_normal((7, 24)).astype(np.float32)
+    y, _ = oracle.blr_forward(**d, x=x)
+    s = float(np.sum(dy.astype(np.float64) * y))
+    dx, [(dh, dl, dg)] = oracle.blr_backward_paths([d], x, dy)
+    scale = float(np.sum(np.abs(dy.astype(np.float64) * y))) + abs(s)
+    for other in (np.sum(x.astype(np.float64) * dx), np.sum(d["h"].astype(np.float64) * dh),
+                  np.sum(d["l"].astype(np.float64) * dl), np.sum(d["g"].astype(np.float64) * dg)):
+        assert abs(other - s) <= 1e-12 * scale
+
+
+def test_blr_backward_dx_is_the_transposed_product_exactly():
+    """dx = dy W^ with W^ = diag(h) S_U diag(l) S_V^T diag(g), summed over two paths, in
+    exact rationals on a tiny layer."""
+    m, d_in, d_out, r = 2, 12, 8, 32
+    paths = [wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=15 + p) for p in range(2)]
+    x = paths[0]["x"]
+    dy = (np.arange(m * d_out, dtype=np.float32).reshape(m, d_out) * np.float32(0.125) - np.float32(0.9))
+    dx, _ = oracle.blr_backward_paths(paths, x, dy)
+    F = lambda v: Fraction(float(v))
+    for t in range(m):
+        for j in range(d_in):
+            exact = Fraction(0)
+            for d in paths:
+                su, sv = _np_signs(d["bits_u"], r), _np_signs(d["bits_v"], r)
+                for i in range(d_out):
+                    w = F(d["h"][i]) * F(d["g"][j]) * sum((int(su[i, k]) * F(d["l"][k]) * int(sv[j, k]) for k in range(r)), Fraction(0))
+                    exact += F(dy[t, i]) * w
+            assert abs(Fraction(dx[t, j]) - exact) <= Fraction(1, 10**9) * (abs(exact) + 1)
