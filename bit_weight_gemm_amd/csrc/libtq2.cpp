@@ -319,7 +319,7 @@ int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v
                        int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
                        size_t workspace_bytes, void *stream) {
     const size_t need = blr_backward_workspace_size(M, d_in, d_out, r);
-    if (need == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 64) return TQ2_EINVAL;  // token chunks fit grid.y
+    if (need == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16) return TQ2_EINVAL;  // token chunks fit grid.y
     int e2 = 0;
     if (!std::isfinite(gscale) || gscale <= 0.0f || std::frexp(gscale, &e2) != 0.5f || gscale > 65536.0f)
         return TQ2_EINVAL;  // a power of two, at most 2^16

@@ -657,9 +657,10 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
 // The two new products read the bitmaps in the other orientation: S_U^T (rows
 // r, contraction d_out) is laid out as S_V is for the forward, and S_V (rows d_in,
 // contraction r) as S_U is.  Column sums over the tokens go in two passes, chunks
-// of kColChunk tokens then the chunks in order, so results do not depend on timing.
+// of kColChunk tokens then the chunks in order, so results do not depend on timing;
+// small chunks give enough threads (columns x chunks) to keep the loads in flight.
 
-constexpr int kColChunk = 64;
+constexpr int kColChunk = 16;
 
 BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrBwdPlan p{};
@@ -718,16 +719,21 @@ __global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
         for (int64_t t = t0; t < t1; ++t) q.H[t * q.ldh + n] = (_Float16)0.0f;
         return;
     }
+    const float *__restrict__ A = q.A;
+    const float *__restrict__ B = q.B;
+    _Float16 *__restrict__ H = q.H;
+    float *__restrict__ D = q.D;
     const float f = q.f[n];
     float sum = 0.0f;
+#pragma unroll 4
     for (int64_t t = t0; t < t1; ++t) {
-        const float a = q.A[t * q.lda + n], b = q.B[t * q.lda + n];
+        const float a = A[t * q.lda + n], b = B[t * q.lda + n];
         sum = sum + a * b;  // product rounded before the sum (no contraction in this kernel)
-        if constexpr (MODE == kColStageH) q.H[t * q.ldh + n] = (_Float16)(a * f * q.gs);
-        if constexpr (MODE == kColDx) q.D[t * q.lda + n] = f * b;
+        if constexpr (MODE == kColStageH) H[t * q.ldh + n] = (_Float16)(a * f * q.gs);
+        if constexpr (MODE == kColDx) D[t * q.lda + n] = f * b;
         if constexpr (MODE == kColDxAcc) {
             const float prod = f * b;
-            q.D[t * q.lda + n] = q.D[t * q.lda + n] + prod;
+            D[t * q.lda + n] = D[t * q.lda + n] + prod;
         }
     }
     q.part[ch * q.N + n] = sum;

@@ -142,13 +142,13 @@ size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64
  * The two new products stage their inputs in f16 as f16(dy.h.gscale) and
  * f16(db.l.gscale) and multiply their f32 results by 1/gscale; gscale must be a
  * power of two in (0, 65536].  a and c are recomputed with the forward's kernels.
- * Sums over tokens are f32 in a fixed order (chunks of 64 tokens, then the chunks
+ * Sums over tokens are f32 in a fixed order (chunks of 16 tokens, then the chunks
  * in order), so results are reproducible.  dh [P][d_out], dl [P][r], dg [P][d_in]
  * are accumulated (y = f32(y + s)); dx [M][d_in] is overwritten by path 0 and the
  * later paths add f32(g.dx') to it.  Operands as for blr_forward_paths, plus dy:
  * device f32 [M][d_out]; all device pointers 4-byte aligned and l 16-byte
  * aligned; outputs must not overlap each other, the inputs or the workspace.
- * M <= 4194240 (65535 chunks of 64 tokens); M == 0 is a no-op.
+ * M <= 1048560 (65535 chunks of 16 tokens); M == 0 is a no-op.
  * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
 int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                        const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
