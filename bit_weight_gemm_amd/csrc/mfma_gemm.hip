@@ -1,4 +1,4 @@
-// Block-tiled MFMA product C[M][N] = f16(A[M][K] * col[K]) x B[N][K]^T on gfx950,
+// Block-tiled MFMA product C[M][N] = f16(A[M][K]) x B[N][K]^T on gfx950,
 // with B read as 2-bit ternary codes and expanded exactly to f16 in registers.
 //
 // Used for
@@ -11,13 +11,20 @@
 //    train_mm.rs", mm_bits): A = f16(x.g) or f16(a.l), B = the sign bitmap
 //    re-laid as codes 0/2 (= -1/+1), no scale.
 //
-// Tiling: a workgroup of WM x WN waves computes a BM x BN tile, stepping K by 64.
-// Each step the workgroup loads the f32 A tile, multiplies by the column factor,
-// rounds to f16 and stores it to a double-buffered, XOR-swizzled LDS tile; each
-// wave then reads its A fragments from LDS (one 16-byte read per 32-row block
-// and 16-wide k slice), loads its B code words straight from memory (one 16-byte
-// load per row and step), decodes them, and issues v_mfma_f32_32x32x16_f16.
-// The next step's global loads are issued before the current step's MFMAs.
+// Tiling: a workgroup of WM x WN x WK waves computes a BM x BN tile.  K is
+// walked in steps of 64*WK*KSUB; k group wk (WM x WN waves) takes KSUB 64-wide
+// slices of each step, and the groups' partial tiles are added through LDS at
+// the end, in group order.  Each step the workgroup loads its A tile (f32 x
+// rounded to f16, or f16 that a producer already rounded) and its B code words
+// and scales, and stores them
+// into STAGES XOR-swizzled LDS buffers; the waves read 16-byte A fragments and
+// B code units from LDS, decode B to exact f16 in registers and issue
+// v_mfma_f32_32x32x16_f16.  Loads run ahead of the LDS stores through ASTG (A)
+// and BDEPTH (B) register stages.
+//
+// The same kernel, with other epilogues, serves the binary low-rank backward
+// (the two gradient products and the recomputation of a and c), below the
+// forward.
 #include <hip/hip_runtime.h>
 
 #include "decode.h"
@@ -34,30 +41,27 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // f16 store (round to nearest even) of the product with a factor per column,
 // 0 past the first nrowf columns; f32 accumulate of the rounded product with a
 // factor per column, C = f32(C + f32(f*v)) (no fused multiply-add); f32 store
-// times one scalar factor alpha.
-enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4 };
+// times one scalar factor alpha; both the plain f32 store (columns below nrowf)
+// and the f16 store of kEpiHalfScale.
+enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4, kEpiStoreHalf = 5 };
 
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
     const _Float16 *Ah;      // [M][lda] f16 (kAHalf)
     int64_t lda;
-    const float *colf;       // [K] per-k factor or nullptr
     const uint32_t *codes;   // [Npad][kw] code words of B
     int64_t kw;
     const uint16_t *scales;  // [Npad][kbw] f16 scales of B, or nullptr
     int64_t kbw;
     float *C;                // [M][ldc]
-    _Float16 *Ch;            // [M][ldc] (kEpiHalfScale)
-    int64_t ldc;
+    _Float16 *Ch;            // [M][ldc] (kEpiHalfScale), [M][ldch] (kEpiStoreHalf)
+    int64_t ldc, ldch;
     const float *rowf;       // [N] output factor (kEpiRowScale, kEpiHalfScale)
     int nrowf;               // factors present (kEpiHalfScale: columns past it get 0)
     float alpha;             // output factor (kEpiScale)
     int M, N, K;             // true sizes; K bounds the A loads
     int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
-    int a_vec;               // A rows and column factors allow 16-byte loads (K % 4 == 0, aligned)
-    int64_t c_slice;         // K slices (grid.y): slice s covers k in [s*Kloop, (s+1)*Kloop) and
-                             // writes its partial product to C + s*c_slice
 };
 
 // LDS has 64 four-byte banks on gfx950: a 16-byte read serves 16 lanes per
@@ -81,20 +85,18 @@ __device__ __forceinline__ int lds_off(int row, int kc) {
 // each group of 16 rows spreads both over all banks.
 __device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15); }
 
-// AMODE: how A tiles are read.  kAExact: K is a multiple of the step and rows
-// past M read row M-1 (ternary GEMM).  kAVec: 16-byte loads with clamped
-// addresses and zeroing past K (needs K % 4 == 0 and 16-byte aligned rows).
-// kAScalar: element-wise guarded loads (any K).  kABuf: as kAExact, but through
-// a buffer resource spanning the M rows, so loads of rows past M return zero
-// without a memory request (small M, M*lda*4 < 2^31).  Rows past M only reach
-// output rows that are never stored.  kAHalf: A already rounded to f16, K a
-// multiple of the step (zero-padded by the producer), rows past M read row M-1.
-enum AMode { kAExact = 0, kAVec = 1, kAScalar = 2, kABuf = 3, kAHalf = 4 };
+// AMODE: how A tiles are read.  kAExact: f32, K is a multiple of the step and
+// rows past M read row M-1 (ternary GEMM).  kABuf: as kAExact, but through a
+// buffer resource spanning the M rows, so loads of rows past M return zero
+// without a memory request (small M, M*lda*4 < 2^31).  kAHalf: A already
+// rounded to f16, K a multiple of the step (zero-padded by the producer), rows
+// past M read row M-1.  Rows past M only reach output rows that are never stored.
+enum AMode { kAExact = 0, kABuf = 3, kAHalf = 4 };
 
 // Workgroup: WK groups of WM x WN waves.  Each step covers SK = 64*WK of K; wave
 // group wk takes the 64-wide slice wk of every step, and the groups' partial
 // tiles are added through LDS at the end (wk = 0, 1, ... in order).
-template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool COLF, bool SCALED,
+template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool SCALED,
           int EPI, int ASTG, int KSUB>
 __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) {
     constexpr int NW = WM * WN;  // waves per k group
@@ -109,7 +111,6 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(STAGES >= 2, "at least two pipeline stages");
     static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
     static_assert(ASTG >= 1 && ASTG <= STAGES && BDEPTH % ASTG == 0, "A register stages");
-    static_assert((AMODE != kABuf && AMODE != kAHalf) || !COLF, "this A mode has no column factors");
     // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds, each taking
     // an equal share of the wave's MB x NB accumulator blocks
     constexpr int RED_ROUNDS = WK == 1 ? 1 : ((WK - 1) * BM * BN * 4 + STAGES * BM * SK * 2 - 1) / (STAGES * BM * SK * 2);
@@ -133,7 +134,6 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     if ((tiles & 7) == 0) tile = (tile & 7) * (tiles >> 3) + (tile >> 3);
     const int m0 = (tile / p.tiles_n) * BM;
     const int n0 = (tile % p.tiles_n) * BN;
-    const int kbase = blockIdx.y * p.Kloop;
 
     f16x acc[MB][NB];
 #pragma unroll
@@ -167,7 +167,6 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     constexpr int PPT = PIECES / T;
     static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
     f4 areg[ASTG][PPT];
-    f4 creg[ASTG][COLF ? PPT : 1];  // column factors of the A pieces (prefetched with them)
     u4 breg[BDEPTH][BPT];
     uint2 dreg[BDEPTH];  // scales of one row quad and block
 
@@ -187,29 +186,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 areg[st][c] = *reinterpret_cast<const f4 *>(p.Ah + (int64_t)gmc * p.lda + gk);  // 8 halves
             } else if constexpr (AMODE == kABuf) {
                 areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (gm * (int)p.lda + gk) * 4, 0, 0));
-            } else if constexpr (AMODE == kAExact) {
-                areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
-                if constexpr (COLF) creg[st][c] = *reinterpret_cast<const f4 *>(p.colf + gk);
-            } else if constexpr (AMODE == kAVec) {
-                // K % 4 == 0: a piece is wholly inside or wholly past K
-                const bool in = gk < p.K;
-                const int gkc = in ? gk : 0;
-                const f4 v = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gkc);
-                areg[st][c] = in ? v : f4{};
-                if constexpr (COLF) {
-                    const f4 cf = *reinterpret_cast<const f4 *>(p.colf + gkc);
-                    creg[st][c] = in ? cf : f4{};
-                }
             } else {
-                f4 v, cf;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool in = gk + e < p.K;
-                    v[e] = (gm < p.M && in) ? p.A[(int64_t)gm * p.lda + gk + e] : 0.0f;
-                    cf[e] = (COLF && in) ? p.colf[gk + e] : 0.0f;
-                }
-                areg[st][c] = v;
-                if constexpr (COLF) creg[st][c] = cf;
+                static_assert(AMODE == kAExact, "A mode");
+                areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
             }
         }
     };
@@ -240,11 +219,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
                 h4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float a = areg[sa][c][e];
-                    if constexpr (COLF) a = a * creg[sa][c][e];  // factors past K are 0
-                    v[e] = (_Float16)a;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = (_Float16)areg[sa][c][e];
                 *reinterpret_cast<h4 *>(&As[st][lds_off<NCH>(row, q >> 1) + ((q & 1) << 2)]) = v;
             }
         }
@@ -309,7 +284,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // step count is a multiple of BDEPTH, so the loop is branch-free; loads and
     // stores past the end use clamped addresses and are never read.
     const int nsteps = p.Kloop / SK;
-    auto clampk = [&](int t) { return kbase + (t < nsteps ? t : nsteps - 1) * SK; };
+    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * SK; };
 #pragma unroll
     for (int st = 0; st < BDEPTH; ++st) {
         if (st < ASTG) load_a(st, clampk(st));
@@ -378,9 +353,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             if (gn >= p.N) continue;
             float rf = 1.0f;
             if constexpr (EPI == kEpiRowScale || EPI == kEpiRowScaleAcc) rf = p.rowf[gn];
-            if constexpr (EPI == kEpiHalfScale) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
+            if constexpr (EPI == kEpiHalfScale || EPI == kEpiStoreHalf) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
             if constexpr (EPI == kEpiScale) rf = p.alpha;
-            float *C = p.C + blockIdx.y * p.c_slice;
+            float *C = p.C;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
@@ -388,6 +363,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                     const float v = acc[mb][nb][r];
                     if constexpr (EPI == kEpiHalfScale) {
                         p.Ch[(int64_t)gm * p.ldc + gn] = (_Float16)(rf * v);
+                    } else if constexpr (EPI == kEpiStoreHalf) {
+                        if (gn < p.nrowf) C[(int64_t)gm * p.ldc + gn] = v;
+                        p.Ch[(int64_t)gm * p.ldch + gn] = (_Float16)(rf * v);
                     } else if constexpr (EPI == kEpiRowScaleAcc) {
                         // two roundings: the product must not be fused into the sum
 #pragma clang fp contract(off)
@@ -401,14 +379,14 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         }
 }
 
-template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool COLF, bool SCALED, int EPI,
+template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool SCALED, int EPI,
           int BDEPTH = STAGES, int ASTG = STAGES, int KSUB = 1>
-static hipError_t run_gemm(GemmArgs p, hipStream_t s, int slices = 1) {
+static hipError_t run_gemm(GemmArgs p, hipStream_t s) {
     p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
-    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, COLF, SCALED, EPI, ASTG, KSUB>
-        <<<dim3((unsigned)tiles, (unsigned)slices), dim3(WM * WN * WK * 64), 0, s>>>(p);
+    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, SCALED, EPI, ASTG, KSUB>
+        <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -420,7 +398,6 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     GemmArgs p{};
     p.A = x;
     p.lda = w.K;
-    p.colf = nullptr;
     p.codes = w.codes;
     p.kw = w.K / 16;
     p.scales = w.scales;
@@ -432,7 +409,6 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     p.N = (int)w.N;
     p.K = (int)w.K;
     p.Kloop = (int)w.K;
-    p.a_vec = 1;
     // K is a multiple of 128 (two steps); four stages when the step count allows
     const bool four = mfma_stages(w.K) == 4;
     // Small M: 64-column tiles whose four waves of each column half split the
@@ -444,23 +420,23 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     // traffic.
     const int64_t kb = w.K / kBlock;
     if (M <= 32 && M * w.K * 4 < ((int64_t)1 << 31)) {
-        if (kb % 8 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, false, true, kEpiStore, 2, 1, 2>(p, s);
-        if (kb % 4 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, false, true, kEpiStore>(p, s);
-        if (kb % 2 == 0) return run_gemm<32, 64, 1, 2, 2, 2, kABuf, false, true, kEpiStore>(p, s);
+        if (kb % 8 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, true, kEpiStore, 2, 1, 2>(p, s);
+        if (kb % 4 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, true, kEpiStore>(p, s);
+        if (kb % 2 == 0) return run_gemm<32, 64, 1, 2, 2, 2, kABuf, true, kEpiStore>(p, s);
     } else if (M <= 64) {
-        if (kb % 8 == 0) return run_gemm<64, 64, 1, 2, 4, 2, kAExact, false, true, kEpiStore, 2, 1, 2>(p, s);
-        if (kb % 4 == 0) return run_gemm<64, 64, 1, 2, 2, 4, kAExact, false, true, kEpiStore>(p, s);
-        if (kb % 2 == 0) return run_gemm<64, 64, 1, 2, 2, 2, kAExact, false, true, kEpiStore>(p, s);
+        if (kb % 8 == 0) return run_gemm<64, 64, 1, 2, 4, 2, kAExact, true, kEpiStore, 2, 1, 2>(p, s);
+        if (kb % 4 == 0) return run_gemm<64, 64, 1, 2, 2, 4, kAExact, true, kEpiStore>(p, s);
+        if (kb % 2 == 0) return run_gemm<64, 64, 1, 2, 2, 2, kAExact, true, kEpiStore>(p, s);
     }
     if (M <= 64)
-        return four ? run_gemm<32, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
-                    : run_gemm<32, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
+        return four ? run_gemm<32, 256, 1, 4, 1, 4, kAExact, true, kEpiStore>(p, s)
+                    : run_gemm<32, 256, 1, 4, 1, 2, kAExact, true, kEpiStore>(p, s);
     // Large M: 128 x 256 tiles of eight waves, two per SIMD: four column waves
     // times two k groups, each k group taking one 64-wide half of a 128-wide
     // step (two LDS buffers, one A register stage).
-    if (kb % 2 == 0) return run_gemm<128, 256, 1, 4, 2, 2, kAExact, false, true, kEpiStore, 2, 1>(p, s);
-    return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, false, true, kEpiStore>(p, s)
-                : run_gemm<128, 256, 1, 4, 1, 2, kAExact, false, true, kEpiStore>(p, s);
+    if (kb % 2 == 0) return run_gemm<128, 256, 1, 4, 2, 2, kAExact, true, kEpiStore, 2, 1>(p, s);
+    return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, true, kEpiStore>(p, s)
+                : run_gemm<128, 256, 1, 4, 1, 2, kAExact, true, kEpiStore>(p, s);
 }
 
 // ------------------------------------------------------------------ binary low-rank forward
@@ -627,22 +603,21 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p1.M = (int)pl.M, p1.N = (int)pl.kpad2, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kpad1;
     hipError_t e;
     if (blr_small_tiles(pl.M, pl.kpad2)) {
-        e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiHalfScale>(p1, s)
-                                      : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiHalfScale>(p1, s);
+        e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiHalfScale>(p1, s)
+                                      : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiHalfScale>(p1, s);
     } else {
-        e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiHalfScale>(p1, s);
+        e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiHalfScale>(p1, s);
     }
     if (e != hipSuccess) return e;
     // GEMM2: c = al . S_U^T, written as y (see below)
     GemmArgs p2{};
-    p2.Ah = al, p2.lda = pl.kpad2, p2.colf = nullptr;
+    p2.Ah = al, p2.lda = pl.kpad2;
     p2.codes = codes_u, p2.kw = pl.kpad2 / 16, p2.scales = nullptr, p2.kbw = 0;
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
     p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.kpad2, p2.Kloop = (int)pl.kpad2;
-    p2.a_vec = 1;
     // y = h . c (later paths of a layer: y = f32(y + f32(h . c)))
-    return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScaleAcc, 2, 1>(p2, s)
-                      : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiRowScale, 2, 1>(p2, s);
+    return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScaleAcc, 2, 1>(p2, s)
+                      : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScale, 2, 1>(p2, s);
 }
 
 // ------------------------------------------------------------------ binary low-rank backward
@@ -653,7 +628,8 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
 //   dx' = (db.l) S_V^T   dg = sum_t x.dx'     dx += g.dx'
 // with the GEMM inputs staged in f16 under a power-of-two gradient scale gs
 // that the GEMM's output factor 1/gs removes again.  a and c are recomputed with
-// the forward's kernels (same tiles, so the same values as the forward's).
+// the forward's kernels and tiles (so with the forward's values); the first
+// product also keeps a in f32 for dl.
 // The two new products read the bitmaps in the other orientation: S_U^T (rows
 // r, contraction d_out) is laid out as S_V is for the forward, and S_V (rows d_in,
 // contraction r) as S_U is.  Column sums over the tokens go in two passes, chunks
@@ -773,6 +749,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     uint32_t *codes_ut = reinterpret_cast<uint32_t *>(at(pb.off_codes_ut));
     uint32_t *codes_vt = reinterpret_cast<uint32_t *>(at(pb.off_codes_vt));
     _Float16 *xg = reinterpret_cast<_Float16 *>(at(pl.off_xg));
+    _Float16 *al = reinterpret_cast<_Float16 *>(at(pl.off_al));
     float *a = reinterpret_cast<float *>(at(pb.off_a));
     float *c = reinterpret_cast<float *>(at(pb.off_c));
     _Float16 *dyh = reinterpret_cast<_Float16 *>(at(pb.off_dyh));
@@ -809,25 +786,25 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         if (e != hipSuccess) return e;
     }
     const bool small = blr_small_tiles(M, pl.kpad2);
-    // a = xg . S_V   [M][r]
+    // a = xg . S_V [M][r] in f32, and al = f16(l.a) [M][kpad2] as the forward's GEMM1 writes it
     {
         GemmArgs p{};
         p.Ah = xg, p.lda = pl.kpad1, p.codes = codes_v, p.kw = pl.kpad1 / 16;
-        p.C = a, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pl.kpad1, p.Kloop = (int)pl.kpad1;
+        p.C = a, p.ldc = r, p.Ch = al, p.ldch = pl.kpad2, p.rowf = l, p.nrowf = (int)r;
+        p.M = (int)M, p.N = (int)pl.kpad2, p.K = (int)pl.kpad1, p.Kloop = (int)pl.kpad1;
         if (small)
-            e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiStore>(p, s)
-                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiStore>(p, s);
+            e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiStoreHalf>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiStoreHalf>(p, s);
         else
-            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiStore>(p, s);
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiStoreHalf>(p, s);
         if (e != hipSuccess) return e;
     }
-    // c = f16(a.l) . S_U^T   [M][d_out]   (a read as f32 and rounded while staged)
+    // c = al . S_U^T   [M][d_out]
     {
         GemmArgs p{};
-        p.A = a, p.lda = r, p.colf = l, p.codes = codes_u, p.kw = pl.kpad2 / 16;
-        p.C = c, p.ldc = d_out, p.M = (int)M, p.N = (int)d_out, p.K = (int)r, p.Kloop = (int)pl.kpad2;
-        p.a_vec = 1;
-        e = run_gemm<64, 128, 1, 4, 2, 2, kAVec, true, false, kEpiStore, 2, 1>(p, s);
+        p.Ah = al, p.lda = pl.kpad2, p.codes = codes_u, p.kw = pl.kpad2 / 16;
+        p.C = c, p.ldc = d_out, p.M = (int)M, p.N = (int)d_out, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiStore, 2, 1>(p, s);
         if (e != hipSuccess) return e;
     }
     // dh += sum_t dy.c, with dyh = f16(dy.h.gs) staged from the same reads
@@ -845,10 +822,10 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         p.C = db, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
         p.alpha = 1.0f / gs;
         if (small)
-            e = (pb.kpado / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, false, kEpiScale>(p, s)
-                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, false, kEpiScale>(p, s);
+            e = (pb.kpado / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiScale>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiScale>(p, s);
         else
-            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, false, kEpiScale>(p, s);
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiScale>(p, s);
         if (e != hipSuccess) return e;
     }
     // dl += sum_t a.db, with dbl = f16(db.l.gs) staged from the same reads
@@ -865,7 +842,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         p.Ah = dbl, p.lda = pl.kpad2, p.codes = codes_vt, p.kw = pl.kpad2 / 16;
         p.C = dxp, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
         p.alpha = 1.0f / gs;
-        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, false, kEpiScale, 2, 1>(p, s);
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiScale, 2, 1>(p, s);
         if (e != hipSuccess) return e;
     }
     // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
