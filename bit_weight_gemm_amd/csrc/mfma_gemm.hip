@@ -720,8 +720,17 @@ __global__ __launch_bounds__(256) void blr_colsum_finish_kernel(const float *__r
                                                                 int64_t N, int64_t chunks) {
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
+    // the loads of a group of chunks are independent: issue them together, then add in order
     float s = 0.0f;
-    for (int64_t ch = 0; ch < chunks; ++ch) s += part[ch * N + n];
+    int64_t ch = 0;
+    for (; ch + 16 <= chunks; ch += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = part[(ch + i) * N + n];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += v[i];
+    }
+    for (; ch < chunks; ++ch) s += part[ch * N + n];
     out[n] = out[n] + s;
 }
 

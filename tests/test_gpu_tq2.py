@@ -162,6 +162,15 @@ def test_results_are_deterministic(torch):
         w.close()
 
 
+@pytest.mark.parametrize("path", ["f32", "mfma"])
+def test_many_rows(torch, path):
+    """M = 300000 rows: the f32 path's grid runs in slices of 65535 row tiles, and the
+    MFMA path has 2344 row tiles; sampled outputs across every slice against the oracle."""
+    aos, n, k = wl.tiny_weight()
+    x = wl.sweep_x(300000, k)
+    check_tq2_sampled(aos, n, k, x, path, "M=300000", count=4096)
+
+
 def test_zero_rows_is_a_noop(torch):
     aos, n, k = wl.tiny_weight()
     w = bw.tq2_upload(aos, n, k)
