@@ -149,6 +149,8 @@ size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64
  * device f32 [M][d_out]; all device pointers 4-byte aligned and l 16-byte
  * aligned; outputs must not overlap each other, the inputs or the workspace.
  * M <= 1048560 (65535 chunks of 16 tokens); M == 0 is a no-op.
+ * Preconditions (not checked): the forward's, and |dy.h.gscale| and |db.l.gscale|
+ * within f16 range (choose gscale so that they are neither huge nor subnormal).
  * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
 int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                        const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
