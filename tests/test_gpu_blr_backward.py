@@ -137,3 +137,26 @@ def test_blr_backward_rejects_bad_gradient_scale(torch):
         _run(paths, x, dy, 3.0)
     with pytest.raises(bw.Tq2Error):
         _run(paths, x, dy, 0.0)
+
+
+def test_blr_backward_rejects_misaligned_and_overlapping_buffers(torch):
+    """l must be 16-byte aligned; dx must not overlap dy or another output."""
+    paths, x, dy = _paths(4, 64, 64, 32, 1, 5)
+    d = paths[0]
+    bu, bv = bits_dev(d["bits_u"][None]), bits_dev(d["bits_v"][None])
+    h, g = to_dev(d["h"][None]), to_dev(d["g"][None])
+    xd, dyd = to_dev(x), to_dev(dy)
+    grads = [torch.zeros((1, n), device="cuda") for n in (64, 32, 64)]
+    l_store = torch.zeros(33 + 3, device="cuda")
+    l_bad = l_store[1:33].view(1, 32)            # 4-byte but not 16-byte aligned
+    l_bad.copy_(to_dev(d["l"][None]))
+    with pytest.raises(bw.Tq2Error):
+        bw.blr_backward_paths(bu, bv, h, l_bad, g, xd, dyd, *grads)
+    l_ok = to_dev(d["l"][None])
+    shared = torch.zeros(4 * 64, device="cuda")
+    with pytest.raises(bw.Tq2Error):              # dx on top of dy
+        bw.blr_backward_paths(bu, bv, h, l_ok, g, xd, shared.view(4, 64), *grads, dx=shared.view(4, 64))
+    with pytest.raises(bw.Tq2Error):              # dh on top of dg
+        both = torch.zeros(64, device="cuda")
+        bw.blr_backward_paths(bu, bv, h, l_ok, g, xd, dyd, both.view(1, 64), grads[1], both.view(1, 64))
+    torch.cuda.synchronize()
