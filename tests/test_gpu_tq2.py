@@ -163,6 +163,24 @@ def test_results_are_deterministic(torch):
 
 
 @pytest.mark.parametrize("path", ["f32", "mfma"])
+@pytest.mark.parametrize("n,k", [(77, 384), (77, 512), (1, 4096), (259, 1024)])
+def test_odd_widths(torch, n, k, path):
+    """N not a multiple of 4 (padded row quads) and a single output row, at M from 1 to
+    past the small-M kernels (M=100), full comparison with the oracle."""
+    aos = wl.sweep_weight(n, k)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for m in (1, 3, 8, 17, 33, 100):
+            x = wl.sweep_x(m, k)
+            note(f"[odd widths] M={m} N={n} K={k} {path}")
+            y = run_tq2(w, x, path)
+            y64, b = oracle.gemm(aos, n, k, x)
+            assert_within(y, y64, b, F32_REL if path == "f32" else MFMA_REL, f"odd widths M={m} N={n} K={k}")
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("path", ["f32", "mfma"])
 def test_many_rows(torch, path):
     """M = 300000 rows: the f32 path's grid runs in slices of 65535 row tiles, and the
     MFMA path has 2344 row tiles; sampled outputs across every slice against the oracle."""
