@@ -365,6 +365,34 @@ def summarize_pmc(fetch_csv, write_csv, kernel, command_fetch, command_write):
         print(f"hbm_bytes_per_launch: {(f_k * ff + w_k * fw) * 1024:.0f}")
 
 
+def summarize_counters(csv_paths, kernel, commands):
+    """Per-dispatch averages of rocprofv3 --pmc counters for one kernel, from one or
+    more counter passes, and the MFMA busy fraction: SQ_VALU_MFMA_BUSY_CYCLES (summed
+    over the chip's 1024 SIMDs; it equals 32 cycles per 32x32x16 MFMA) over the
+    GPU-active cycles of one XCD (GRBM_GUI_ACTIVE reads the sum over the 8 XCDs)."""
+    import csv
+
+    vals = {}
+    for path in csv_paths.split(","):
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    print("# rocprofv3 counters per dispatch")
+    for c in commands.split(";;"):
+        print(f"# command: {c.strip()}")
+    print(f"kernel: {kernel}")
+    for name in sorted(vals):
+        v = vals[name]
+        print(f"{name}: {sum(v) / len(v):.6g}   (dispatches: {len(v)})")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        print(f"mfma_busy_fraction: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (avg['GRBM_GUI_ACTIVE'] / 8 * 1024):.4f}")
+    if "SQ_INSTS_MFMA" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        print(f"mfma_busy_cycles_per_mfma_instruction: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_INSTS_MFMA']:.2f}")
+    if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+        print(f"wave_cycles_waiting_fraction: {avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.4f}")
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the decode workload."""
     import oracle
@@ -396,7 +424,12 @@ def main():
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "CMD_F", "CMD_W"),
                     help="print HBM traffic per launch from two counter runs and exit")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("CSVS", "KERNEL", "COMMANDS"),
+                    help="print per-dispatch counter averages of KERNEL (CSVs comma-separated, commands ';;'-separated)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
         return
