@@ -98,3 +98,15 @@ def test_blr_forward_rejects_bad_sizes_on_the_host(L):
     # a layer needs at least one path; bad sizes are refused as for one path
     assert L.blr_forward_paths(0, None, None, None, None, None, None, None, 4, 8, 8, 32, None, 0, None) == bw.TQ2_EINVAL
     assert L.blr_forward_paths(2, None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
