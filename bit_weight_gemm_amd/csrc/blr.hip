@@ -1,0 +1,433 @@
+// Binary low-rank layer ("cortiq-engine 0.8.43 -- train_mm.rs", module header,
+// blr_forward / blr_backward): the sign bitmaps re-laid as 2-bit codes, and the
+// layer's products on the block-tiled MFMA kernel of mfma_gemm.h.
+#include "mfma_gemm.h"
+
+namespace tq2 {
+
+// ------------------------------------------------------------------ binary low-rank forward
+
+static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Tiles of the two products.  The preparation pass re-lays both bitmaps and
+// writes f16(x*g) (the A operand of GEMM1, zero-padded in K).  GEMM1 (M x r,
+// K = d_in) writes f16(l * a), the A operand of GEMM2 (M x d_out, K = r), from
+// its epilogue; its columns past r are zero.  Small M takes 32 x 64 tiles of
+// GEMM1 (eight waves, four k groups) so that enough workgroups stream the long
+// K without splitting it; larger M takes 128 x 128 tiles.
+constexpr int kBlrKPad = 512;     // GEMM1's K padding: whole pipeline rounds of either tile
+constexpr int kBlr2Step = 2 * 2 * BK;  // GEMM2: two k groups x 64, two stages
+
+static bool blr_small_tiles(int64_t M, int64_t kpad2) { return ((M + 31) / 32) * (kpad2 / 64) < 2048; }
+
+BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    BlrPlan p{};
+    p.M = M, p.d_in = d_in, p.d_out = d_out, p.r = r;
+    p.kpad1 = round_up(d_in, kBlrKPad);
+    p.kpad2 = round_up(r, kBlr2Step);
+    p.npad1 = round_up(r, kRowPad);
+    p.npad2 = round_up(d_out, kRowPad);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return at;
+    };
+    p.off_codes_v = take((size_t)p.npad1 * (p.kpad1 / 16) * 4);
+    p.off_codes_u = take((size_t)p.npad2 * (p.kpad2 / 16) * 4);
+    p.off_al = take((size_t)M * p.kpad2 * 2);
+    p.off_xg = take((size_t)M * p.kpad1 * 2);
+    p.total = off;
+    return p;
+}
+
+// Sign bitmaps -> code words (set bit -> code 2 = +1, clear -> code 0 = -1,
+// padding -> code 1 = 0) in the device layout, with row index n and
+// contraction index k, for both matrices in one launch.  A thread makes the
+// 16-byte unit of four rows (4q .. 4q+3) for one 16-wide k group g.
+//   S_V: sign(n, k) = bit n of bits_v[k][n/32]   (n = rank, k = input j): a wave
+//        takes 64 consecutive row quads of one group, so each of its 16 loads
+//        (one per k) touches 8 bitmap words shared by the lanes;
+//   S_U: sign(n, k) = bit k of bits_u[n][k/32]   (n = output i, k = rank): a
+//        wave takes 64 consecutive groups of one row quad, so its loads read
+//        whole bitmap rows and its stores are contiguous.
+// Out-of-range elements read a valid word and are replaced by code 1.
+// Blocks from nblk_v + nblk_u on write xg[m][k] = f16(x[m][k] * g[k]) (product in
+// f32, round to nearest even) for k < d_in and 0 up to kpad1, 8 values per thread.
+struct BlrPrep {
+    const uint32_t *bits_v, *bits_u;
+    uint32_t *codes_v, *codes_u;
+    const float *x, *g;
+    _Float16 *xg;
+    int64_t words;                     // r / 32
+    int64_t M, r, d_in, d_out;
+    int64_t npad1, kpad1, npad2, kpad2;
+    int64_t nblk_v, nblk_u;
+    int xvec;                          // x rows and g allow 16-byte loads
+};
+
+// code of element e (0..15) at its place in a group word
+__device__ __forceinline__ uint32_t code_at(uint32_t code, int e) { return code << (2 * (e >> 1) + 16 * (e & 1)); }
+
+__global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
+    const int64_t bid = blockIdx.x;
+    if (bid < q.nblk_v) {
+        const int64_t kw = q.kpad1 / 16, quads = q.npad1 / 4;
+        const int64_t qblocks = (quads + 255) / 256;
+        const int64_t quad = (bid % qblocks) * 256 + threadIdx.x, g = bid / qblocks;
+        if (quad >= quads) return;
+        const int64_t n0 = quad * 4;
+        const bool nin = n0 < q.r;  // r % 32 == 0: a quad is wholly inside or wholly past r
+        const int64_t wrd = nin ? n0 >> 5 : 0;
+        const int sh = (int)(n0 & 31);
+        u4 out = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t k = g * 16 + e;
+            const bool in = nin && k < q.d_in;
+            const uint32_t bits = (q.bits_v[(in ? k : 0) * q.words + wrd] >> sh) & 15u;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                out[rr] |= code_at(in ? (((bits >> rr) & 1u) ? 2u : 0u) : 1u, e);
+        }
+        *reinterpret_cast<u4 *>(q.codes_v + (quad * kw + g) * 4) = out;
+    } else if (bid < q.nblk_v + q.nblk_u) {
+        const int64_t kw = q.kpad2 / 16;
+        const int64_t gblocks = (kw + 255) / 256;
+        const int64_t rel = bid - q.nblk_v;
+        const int64_t quad = rel / gblocks, g = (rel % gblocks) * 256 + threadIdx.x;
+        if (g >= kw) return;
+        u4 out;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t n = quad * 4 + rr;
+            const bool in = n < q.d_out && g * 16 < q.r;
+            const uint32_t half = (q.bits_u[(in ? n : 0) * q.words + (in ? g >> 1 : 0)] >> (16 * (g & 1))) & 0xFFFFu;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const bool ine = in && g * 16 + e < q.r;
+                w |= code_at(ine ? (((half >> e) & 1u) ? 2u : 0u) : 1u, e);
+            }
+            out[rr] = w;
+        }
+        *reinterpret_cast<u4 *>(q.codes_u + (quad * kw + g) * 4) = out;
+    } else {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const int64_t per_row = q.kpad1 / 8;
+        const int64_t piece = (bid - q.nblk_v - q.nblk_u) * 256 + threadIdx.x;
+        if (piece >= q.M * per_row) return;
+        const int64_t m = piece / per_row, k0 = (piece % per_row) * 8;
+        const float *xr = q.x + m * q.d_in;
+        h8 out;
+        if (q.xvec && k0 + 8 <= q.d_in) {
+            const f4 x0 = *reinterpret_cast<const f4 *>(xr + k0), x1 = *reinterpret_cast<const f4 *>(xr + k0 + 4);
+            const f4 g0 = *reinterpret_cast<const f4 *>(q.g + k0), g1 = *reinterpret_cast<const f4 *>(q.g + k0 + 4);
+            const f4 p0 = x0 * g0, p1 = x1 * g1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (_Float16)p0[e], out[e + 4] = (_Float16)p1[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t k = k0 + e;
+                out[e] = (_Float16)(k < q.d_in ? xr[k] * q.g[k] : 0.0f);
+            }
+        }
+        *reinterpret_cast<h8 *>(q.xg + m * q.kpad1 + k0) = out;
+    }
+}
+
+hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
+                              const float *h, const float *l, const float *g, const float *x, float *y,
+                              void *workspace, bool accumulate, hipStream_t s) {
+    char *ws = static_cast<char *>(workspace);
+    uint32_t *codes_v = reinterpret_cast<uint32_t *>(ws + pl.off_codes_v);
+    uint32_t *codes_u = reinterpret_cast<uint32_t *>(ws + pl.off_codes_u);
+    _Float16 *al = reinterpret_cast<_Float16 *>(ws + pl.off_al);
+    _Float16 *xg = reinterpret_cast<_Float16 *>(ws + pl.off_xg);
+    {
+        BlrPrep q{};
+        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
+        q.x = x, q.g = g, q.xg = xg;
+        q.words = pl.r / 32, q.M = pl.M, q.r = pl.r, q.d_in = pl.d_in, q.d_out = pl.d_out;
+        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
+        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
+        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.xvec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+        const int64_t nblk_x = (pl.M * (pl.kpad1 / 8) + 255) / 256;
+        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // GEMM1: al[M][kpad2] = f16(l . (xg . S_V)); rows of S_V past r are code 1, so
+    // the padded columns come out as 0 (and their factor is 0)
+    GemmArgs p1{};
+    p1.Ah = xg, p1.lda = pl.kpad1;
+    p1.codes = codes_v, p1.kw = pl.kpad1 / 16, p1.scales = nullptr, p1.kbw = 0;
+    p1.Ch = al, p1.ldc = pl.kpad2, p1.rowf = l, p1.nrowf = (int)pl.r;
+    p1.M = (int)pl.M, p1.N = (int)pl.kpad2, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kpad1;
+    hipError_t e;
+    if (blr_small_tiles(pl.M, pl.kpad2)) {
+        e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiHalfScale>(p1, s)
+                                      : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiHalfScale>(p1, s);
+    } else {
+        e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiHalfScale>(p1, s);
+    }
+    if (e != hipSuccess) return e;
+    // GEMM2: c = al . S_U^T, written as y (see below)
+    GemmArgs p2{};
+    p2.Ah = al, p2.lda = pl.kpad2;
+    p2.codes = codes_u, p2.kw = pl.kpad2 / 16, p2.scales = nullptr, p2.kbw = 0;
+    p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
+    p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.kpad2, p2.Kloop = (int)pl.kpad2;
+    // y = h . c (later paths of a layer: y = f32(y + f32(h . c)))
+    return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScaleAcc, 2, 1>(p2, s)
+                      : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScale, 2, 1>(p2, s);
+}
+
+// ------------------------------------------------------------------ binary low-rank backward
+//
+// "cortiq-engine 0.8.43 -- train_mm.rs", module header: for a path with
+// a = (x.g) S_V and c = (a.l) S_U^T,
+//   dh = sum_t dy.c      db = (dy.h) S_U      dl = sum_t a.db
+//   dx' = (db.l) S_V^T   dg = sum_t x.dx'     dx += g.dx'
+// with the GEMM inputs staged in f16 under a power-of-two gradient scale gs
+// that the GEMM's output factor 1/gs removes again.  a and c are recomputed with
+// the forward's kernels and tiles (so with the forward's values); the first
+// product also keeps a in f32 for dl.
+// The two new products read the bitmaps in the other orientation: S_U^T (rows
+// r, contraction d_out) is laid out as S_V is for the forward, and S_V (rows d_in,
+// contraction r) as S_U is.  Column sums over the tokens go in two passes, chunks
+// of kColChunk tokens then the chunks in order, so results do not depend on timing;
+// small chunks give enough threads (columns x chunks) to keep the loads in flight.
+
+constexpr int kColChunk = 16;
+
+BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    BlrBwdPlan p{};
+    p.fwd = blr_plan(M, d_in, d_out, r);
+    p.kpado = round_up(d_out, kBlrKPad);
+    p.npadi = round_up(d_in, kRowPad);
+    p.chunks = (M + kColChunk - 1) / kColChunk;
+    const int64_t widest = d_in > d_out ? (d_in > r ? d_in : r) : (d_out > r ? d_out : r);
+    size_t off = p.fwd.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return at;
+    };
+    p.off_codes_ut = take((size_t)p.fwd.npad1 * (p.kpado / 16) * 4);
+    p.off_codes_vt = take((size_t)p.npadi * (p.fwd.kpad2 / 16) * 4);
+    p.off_a = take((size_t)M * r * 4);
+    p.off_c = take((size_t)M * d_out * 4);
+    p.off_dyh = take((size_t)M * p.kpado * 2);
+    p.off_db = take((size_t)M * r * 4);
+    p.off_dbl = take((size_t)M * p.fwd.kpad2 * 2);
+    p.off_dxp = take((size_t)M * d_in * 4);
+    p.off_part = take((size_t)(p.chunks > 0 ? p.chunks : 1) * widest * 4);
+    p.total = off;
+    return p;
+}
+
+namespace {
+
+enum ColMode { kColStageH = 0, kColDx = 1, kColDxAcc = 2 };
+
+// Pass 1 of a column sum: part[ch][n] = sum over tokens t of chunk ch of
+// A[t][n] * B[t][n] (f32, ascending t), for n < N.  Fused with the elementwise
+// op that reads the same operand A:
+//   kColStageH: H[t][n] = f16(A[t][n] * f[n] * gs) for n < N, 0 for N <= n < ldh;
+//   kColDx:     D[t][n] = f[n] * B[t][n];
+//   kColDxAcc:  D[t][n] = f32(D[t][n] + f32(f[n] * B[t][n])).
+struct ColArgs {
+    const float *A, *B, *f;
+    float *part;
+    _Float16 *H;
+    float *D;
+    int64_t M, N, lda, ldh;
+    float gs;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
+#pragma clang fp contract(off)
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t ch = blockIdx.y;
+    const int64_t t0 = ch * kColChunk, t1 = t0 + kColChunk < q.M ? t0 + kColChunk : q.M;
+    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
+    if (n >= ncols) return;
+    if (n >= q.N) {  // padding columns of the staged operand
+        for (int64_t t = t0; t < t1; ++t) q.H[t * q.ldh + n] = (_Float16)0.0f;
+        return;
+    }
+    const float *__restrict__ A = q.A;
+    const float *__restrict__ B = q.B;
+    _Float16 *__restrict__ H = q.H;
+    float *__restrict__ D = q.D;
+    const float f = q.f[n];
+    float sum = 0.0f;
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+        const float a = A[t * q.lda + n], b = B[t * q.lda + n];
+        sum = sum + a * b;  // product rounded before the sum (no contraction in this kernel)
+        if constexpr (MODE == kColStageH) H[t * q.ldh + n] = (_Float16)(a * f * q.gs);
+        if constexpr (MODE == kColDx) D[t * q.lda + n] = f * b;
+        if constexpr (MODE == kColDxAcc) {
+            const float prod = f * b;
+            D[t * q.lda + n] = D[t * q.lda + n] + prod;
+        }
+    }
+    q.part[ch * q.N + n] = sum;
+}
+
+// Pass 2: out[n] = f32(out[n] + f32(sum over chunks in order of part[ch][n])).
+__global__ __launch_bounds__(256) void blr_colsum_finish_kernel(const float *__restrict__ part, float *__restrict__ out,
+                                                                int64_t N, int64_t chunks) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    // the loads of a group of chunks are independent: issue them together, then add in order
+    float s = 0.0f;
+    int64_t ch = 0;
+    for (; ch + 16 <= chunks; ch += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = part[(ch + i) * N + n];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += v[i];
+    }
+    for (; ch < chunks; ++ch) s += part[ch * N + n];
+    out[n] = out[n] + s;
+}
+
+template <int MODE>
+hipError_t colsum(const ColArgs &q, float *out, int64_t chunks, hipStream_t s) {
+    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
+    blr_colsum_kernel<MODE><<<dim3((unsigned)((ncols + 255) / 256), (unsigned)chunks), dim3(256), 0, s>>>(q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    blr_colsum_finish_kernel<<<dim3((unsigned)((q.N + 255) / 256)), dim3(256), 0, s>>>(q.part, out, q.N, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                               const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                               float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s) {
+    const BlrPlan &pl = pb.fwd;
+    const int64_t M = pl.M, d_in = pl.d_in, d_out = pl.d_out, r = pl.r;
+    char *ws = static_cast<char *>(workspace);
+    auto at = [&](size_t off) { return ws + off; };
+    uint32_t *codes_v = reinterpret_cast<uint32_t *>(at(pl.off_codes_v));
+    uint32_t *codes_u = reinterpret_cast<uint32_t *>(at(pl.off_codes_u));
+    uint32_t *codes_ut = reinterpret_cast<uint32_t *>(at(pb.off_codes_ut));
+    uint32_t *codes_vt = reinterpret_cast<uint32_t *>(at(pb.off_codes_vt));
+    _Float16 *xg = reinterpret_cast<_Float16 *>(at(pl.off_xg));
+    _Float16 *al = reinterpret_cast<_Float16 *>(at(pl.off_al));
+    float *a = reinterpret_cast<float *>(at(pb.off_a));
+    float *c = reinterpret_cast<float *>(at(pb.off_c));
+    _Float16 *dyh = reinterpret_cast<_Float16 *>(at(pb.off_dyh));
+    float *db = reinterpret_cast<float *>(at(pb.off_db));
+    _Float16 *dbl = reinterpret_cast<_Float16 *>(at(pb.off_dbl));
+    float *dxp = reinterpret_cast<float *>(at(pb.off_dxp));
+    float *part = reinterpret_cast<float *>(at(pb.off_part));
+    hipError_t e;
+    // bitmaps in both orientations, and f16(x.g)
+    {
+        BlrPrep q{};
+        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
+        q.x = x, q.g = g, q.xg = xg;
+        q.words = r / 32, q.M = M, q.r = r, q.d_in = d_in, q.d_out = d_out;
+        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
+        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
+        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.xvec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+        const int64_t nblk_x = (M * (pl.kpad1 / 8) + 255) / 256;
+        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // S_U^T: rows r, contraction d_out (bits along the rows, as S_V's);
+        // S_V: rows d_in, contraction r (bits along the contraction, as S_U's)
+        BlrPrep t{};
+        t.bits_v = bits_u, t.codes_v = codes_ut, t.d_in = d_out, t.kpad1 = pb.kpado, t.npad1 = pl.npad1;
+        t.bits_u = bits_v, t.codes_u = codes_vt, t.d_out = d_in, t.kpad2 = pl.kpad2, t.npad2 = pb.npadi;
+        t.words = r / 32, t.M = 0, t.r = r;
+        t.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pb.kpado / 16);
+        t.nblk_u = (pb.npadi / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        blr_prep_kernel<<<dim3((unsigned)(t.nblk_v + t.nblk_u)), dim3(256), 0, s>>>(t);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const bool small = blr_small_tiles(M, pl.kpad2);
+    // a = xg . S_V [M][r] in f32, and al = f16(l.a) [M][kpad2] as the forward's GEMM1 writes it
+    {
+        GemmArgs p{};
+        p.Ah = xg, p.lda = pl.kpad1, p.codes = codes_v, p.kw = pl.kpad1 / 16;
+        p.C = a, p.ldc = r, p.Ch = al, p.ldch = pl.kpad2, p.rowf = l, p.nrowf = (int)r;
+        p.M = (int)M, p.N = (int)pl.kpad2, p.K = (int)pl.kpad1, p.Kloop = (int)pl.kpad1;
+        if (small)
+            e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiStoreHalf>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiStoreHalf>(p, s);
+        else
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiStoreHalf>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // c = al . S_U^T   [M][d_out]
+    {
+        GemmArgs p{};
+        p.Ah = al, p.lda = pl.kpad2, p.codes = codes_u, p.kw = pl.kpad2 / 16;
+        p.C = c, p.ldc = d_out, p.M = (int)M, p.N = (int)d_out, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiStore, 2, 1>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dh += sum_t dy.c, with dyh = f16(dy.h.gs) staged from the same reads
+    {
+        ColArgs q{};
+        q.A = dy, q.B = c, q.f = h, q.part = part, q.H = dyh, q.M = M, q.N = d_out, q.lda = d_out, q.ldh = pb.kpado;
+        q.gs = gs;
+        e = colsum<kColStageH>(q, dh, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    // db = dyh . S_U / gs   [M][r]
+    {
+        GemmArgs p{};
+        p.Ah = dyh, p.lda = pb.kpado, p.codes = codes_ut, p.kw = pb.kpado / 16;
+        p.C = db, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
+        p.alpha = 1.0f / gs;
+        if (small)
+            e = (pb.kpado / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiScale>(p, s)
+                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiScale>(p, s);
+        else
+            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiScale>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dl += sum_t a.db, with dbl = f16(db.l.gs) staged from the same reads
+    {
+        ColArgs q{};
+        q.A = db, q.B = a, q.f = l, q.part = part, q.H = dbl, q.M = M, q.N = r, q.lda = r, q.ldh = pl.kpad2;
+        q.gs = gs;
+        e = colsum<kColStageH>(q, dl, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    // dx' = dbl . S_V^T / gs   [M][d_in]
+    {
+        GemmArgs p{};
+        p.Ah = dbl, p.lda = pl.kpad2, p.codes = codes_vt, p.kw = pl.kpad2 / 16;
+        p.C = dxp, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
+        p.alpha = 1.0f / gs;
+        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiScale, 2, 1>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
+    {
+        ColArgs q{};
+        q.A = x, q.B = dxp, q.f = g, q.part = part, q.D = dx, q.M = M, q.N = d_in, q.lda = d_in;
+        e = accumulate_dx ? colsum<kColDxAcc>(q, dg, pb.chunks, s) : colsum<kColDx>(q, dg, pb.chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace tq2
