@@ -475,7 +475,7 @@ def main():
         out["blr"] = bench_blr(torch, bw, max(K // 10, 20), max(W // 5, 5))
         log(f"[blr] {json.dumps(out['blr'])}")
         out["blr_backward"] = bench_blr_backward(torch, bw, max(K // 20, 20), max(W // 5, 5))
-        log(f"[blr] {json.dumps(out['blr'])}")
+        log(f"[blr backward] {json.dumps(out['blr_backward'])}")
 
     line = {
         "metric": "TQ2 GEMM weight-GB/s (M=1) and TFLOP/s (M=2048), % of HBM/MFMA roofline",

@@ -20,6 +20,23 @@ constexpr int kBlr2Step = 2 * 2 * BK;  // GEMM2: two k groups x 64, two stages
 
 static bool blr_small_tiles(int64_t M, int64_t kpad2) { return ((M + 31) / 32) * (kpad2 / 64) < 2048; }
 
+// Products with the long contraction (GEMM1 over d_in, and the backward's db over
+// d_out), of M x r outputs: 32 x 64 tiles when they are few, each wave taking two
+// 64-wide slices of a 512-wide step when the padded contraction allows (fewer
+// steps and barriers), else 128 x 128 tiles.
+template <int EPI>
+static hipError_t gemm_long_k(const GemmArgs &p, int64_t kpad, bool small, hipStream_t s) {
+    if (!small) return run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, EPI>(p, s);
+    if (kpad % 1024 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, EPI, 2, 1, 2>(p, s);
+    return run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, EPI>(p, s);
+}
+// Products with the short contraction r (GEMM2, and the backward's dx'): 64 x 128
+// tiles of eight waves (two k groups), A loaded two steps ahead.
+template <int EPI>
+static hipError_t gemm_short_k(const GemmArgs &p, hipStream_t s) {
+    return run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, EPI, 2, 2>(p, s);
+}
+
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrPlan p{};
     p.M = M, p.d_in = d_in, p.d_out = d_out, p.r = r;
@@ -48,9 +65,9 @@ BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 //   S_V: sign(n, k) = bit n of bits_v[k][n/32]   (n = rank, k = input j): a wave
 //        takes 64 consecutive row quads of one group, so each of its 16 loads
 //        (one per k) touches 8 bitmap words shared by the lanes;
-//   S_U: sign(n, k) = bit k of bits_u[n][k/32]   (n = output i, k = rank): a
-//        wave takes 64 consecutive groups of one row quad, so its loads read
-//        whole bitmap rows and its stores are contiguous.
+//   S_U: sign(n, k) = bit k of bits_u[n][k/32]   (n = output i, k = rank): the
+//        threads walk (row quad, group) with the group fastest, so a wave's
+//        loads read whole bitmap rows and its stores are contiguous.
 // Out-of-range elements read a valid word and are replaced by code 1.
 // Blocks from nblk_v + nblk_u on write xg[m][k] = f16(x[m][k] * g[k]) (product in
 // f32, round to nearest even) for k < d_in and 0 up to kpad1, 8 values per thread.
@@ -93,10 +110,9 @@ __global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
         *reinterpret_cast<u4 *>(q.codes_v + (quad * kw + g) * 4) = out;
     } else if (bid < q.nblk_v + q.nblk_u) {
         const int64_t kw = q.kpad2 / 16;
-        const int64_t gblocks = (kw + 255) / 256;
-        const int64_t rel = bid - q.nblk_v;
-        const int64_t quad = rel / gblocks, g = (rel % gblocks) * 256 + threadIdx.x;
-        if (g >= kw) return;
+        const int64_t item = (bid - q.nblk_v) * 256 + threadIdx.x;
+        if (item >= (q.npad2 / 4) * kw) return;
+        const int64_t quad = item / kw, g = item % kw;
         u4 out;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -152,7 +168,7 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
         q.words = pl.r / 32, q.M = pl.M, q.r = pl.r, q.d_in = pl.d_in, q.d_out = pl.d_out;
         q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
         q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
-        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.nblk_u = ((pl.npad2 / 4) * (pl.kpad2 / 16) + 255) / 256;
         q.xvec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
                  ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
         const int64_t nblk_x = (pl.M * (pl.kpad1 / 8) + 255) / 256;
@@ -168,12 +184,7 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p1.Ch = al, p1.ldc = pl.kpad2, p1.rowf = l, p1.nrowf = (int)pl.r;
     p1.M = (int)pl.M, p1.N = (int)pl.kpad2, p1.K = (int)pl.kpad1, p1.Kloop = (int)pl.kpad1;
     hipError_t e;
-    if (blr_small_tiles(pl.M, pl.kpad2)) {
-        e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiHalfScale>(p1, s)
-                                      : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiHalfScale>(p1, s);
-    } else {
-        e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiHalfScale>(p1, s);
-    }
+    e = gemm_long_k<kEpiHalfScale>(p1, pl.kpad1, blr_small_tiles(pl.M, pl.kpad2), s);
     if (e != hipSuccess) return e;
     // GEMM2: c = al . S_U^T, written as y (see below)
     GemmArgs p2{};
@@ -182,8 +193,7 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
     p2.M = (int)pl.M, p2.N = (int)pl.d_out, p2.K = (int)pl.kpad2, p2.Kloop = (int)pl.kpad2;
     // y = h . c (later paths of a layer: y = f32(y + f32(h . c)))
-    return accumulate ? run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScaleAcc, 2, 1>(p2, s)
-                      : run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiRowScale, 2, 1>(p2, s);
+    return accumulate ? gemm_short_k<kEpiRowScaleAcc>(p2, s) : gemm_short_k<kEpiRowScale>(p2, s);
 }
 
 // ------------------------------------------------------------------ binary low-rank backward
@@ -341,7 +351,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         q.words = r / 32, q.M = M, q.r = r, q.d_in = d_in, q.d_out = d_out;
         q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
         q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
-        q.nblk_u = (pl.npad2 / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        q.nblk_u = ((pl.npad2 / 4) * (pl.kpad2 / 16) + 255) / 256;
         q.xvec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
                  ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
         const int64_t nblk_x = (M * (pl.kpad1 / 8) + 255) / 256;
@@ -355,7 +365,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         t.bits_u = bits_v, t.codes_u = codes_vt, t.d_out = d_in, t.kpad2 = pl.kpad2, t.npad2 = pb.npadi;
         t.words = r / 32, t.M = 0, t.r = r;
         t.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pb.kpado / 16);
-        t.nblk_u = (pb.npadi / 4) * ((pl.kpad2 / 16 + 255) / 256);
+        t.nblk_u = ((pb.npadi / 4) * (pl.kpad2 / 16) + 255) / 256;
         blr_prep_kernel<<<dim3((unsigned)(t.nblk_v + t.nblk_u)), dim3(256), 0, s>>>(t);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -367,11 +377,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         p.Ah = xg, p.lda = pl.kpad1, p.codes = codes_v, p.kw = pl.kpad1 / 16;
         p.C = a, p.ldc = r, p.Ch = al, p.ldch = pl.kpad2, p.rowf = l, p.nrowf = (int)r;
         p.M = (int)M, p.N = (int)pl.kpad2, p.K = (int)pl.kpad1, p.Kloop = (int)pl.kpad1;
-        if (small)
-            e = (pl.kpad1 / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiStoreHalf>(p, s)
-                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiStoreHalf>(p, s);
-        else
-            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiStoreHalf>(p, s);
+        e = gemm_long_k<kEpiStoreHalf>(p, pl.kpad1, small, s);
         if (e != hipSuccess) return e;
     }
     // c = al . S_U^T   [M][d_out]
@@ -379,7 +385,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         GemmArgs p{};
         p.Ah = al, p.lda = pl.kpad2, p.codes = codes_u, p.kw = pl.kpad2 / 16;
         p.C = c, p.ldc = d_out, p.M = (int)M, p.N = (int)d_out, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
-        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiStore, 2, 1>(p, s);
+        e = gemm_short_k<kEpiStore>(p, s);
         if (e != hipSuccess) return e;
     }
     // dh += sum_t dy.c, with dyh = f16(dy.h.gs) staged from the same reads
@@ -396,11 +402,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         p.Ah = dyh, p.lda = pb.kpado, p.codes = codes_ut, p.kw = pb.kpado / 16;
         p.C = db, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
         p.alpha = 1.0f / gs;
-        if (small)
-            e = (pb.kpado / 256) % 4 == 0 ? run_gemm<32, 64, 1, 2, 4, 4, kAHalf, false, kEpiScale>(p, s)
-                                          : run_gemm<32, 64, 1, 2, 4, 2, kAHalf, false, kEpiScale>(p, s);
-        else
-            e = run_gemm<128, 128, 1, 4, 1, 4, kAHalf, false, kEpiScale>(p, s);
+        e = gemm_long_k<kEpiScale>(p, pb.kpado, small, s);
         if (e != hipSuccess) return e;
     }
     // dl += sum_t a.db, with dbl = f16(db.l.gs) staged from the same reads
@@ -417,7 +419,7 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         p.Ah = dbl, p.lda = pl.kpad2, p.codes = codes_vt, p.kw = pl.kpad2 / 16;
         p.C = dxp, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
         p.alpha = 1.0f / gs;
-        e = run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, kEpiScale, 2, 1>(p, s);
+        e = gemm_short_k<kEpiScale>(p, s);
         if (e != hipSuccess) return e;
     }
     // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))

@@ -43,8 +43,11 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // 0 past the first nrowf columns; f32 accumulate of the rounded product with a
 // factor per column, C = f32(C + f32(f*v)) (no fused multiply-add); f32 store
 // times one scalar factor alpha; both the plain f32 store (columns below nrowf)
-// and the f16 store of kEpiHalfScale.
-enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4, kEpiStoreHalf = 5 };
+// and the f16 store of kEpiHalfScale; the plain f32 store marked non-temporal
+// (for outputs of tens of MB that this kernel never reads back: they then take
+// less of the caches that the A and B tiles stream through).
+enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4, kEpiStoreHalf = 5,
+           kEpiStoreNT = 6 };
 
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
@@ -373,6 +376,8 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                         float *c = C + (int64_t)gm * p.ldc + gn;
                         const float prod = rf * v;
                         *c = *c + prod;
+                    } else if constexpr (EPI == kEpiStoreNT) {
+                        __builtin_nontemporal_store(v, &C[(int64_t)gm * p.ldc + gn]);
                     } else
                         C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale || EPI == kEpiScale) ? rf * v : v;
                 }

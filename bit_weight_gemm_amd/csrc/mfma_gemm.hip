@@ -46,10 +46,11 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
                     : run_gemm<32, 256, 1, 4, 1, 2, kAExact, true, kEpiStore>(p, s);
     // Large M: 128 x 256 tiles of eight waves, two per SIMD: four column waves
     // times two k groups, each k group taking one 64-wide half of a 128-wide
-    // step (two LDS buffers, one A register stage).
-    if (kb % 2 == 0) return run_gemm<128, 256, 1, 4, 2, 2, kAExact, true, kEpiStore, 2, 1>(p, s);
-    return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, true, kEpiStore>(p, s)
-                : run_gemm<128, 256, 1, 4, 1, 2, kAExact, true, kEpiStore>(p, s);
+    // step (two LDS buffers, one A register stage).  y (32 MB at M=2048,
+    // N=4096) is stored non-temporally.
+    if (kb % 2 == 0) return run_gemm<128, 256, 1, 4, 2, 2, kAExact, true, kEpiStoreNT, 2, 1>(p, s);
+    return four ? run_gemm<128, 256, 1, 4, 1, 4, kAExact, true, kEpiStoreNT>(p, s)
+                : run_gemm<128, 256, 1, 4, 1, 2, kAExact, true, kEpiStoreNT>(p, s);
 }
 
 }  // namespace tq2
