@@ -47,7 +47,7 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
 
 // Skinny MFMA kernel for M <= kSkinnyMaxM whose x (as f16) fits in LDS.
 constexpr int64_t kSkinnyMaxM = 16;
-constexpr size_t kSkinnyMaxLds = 128 * 1024;
+constexpr size_t kSkinnyMaxLds = 160 * 1024;  // all of gfx950's LDS per workgroup
 bool skinny_fits(const DevWeight &w, int64_t M);
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s);
 

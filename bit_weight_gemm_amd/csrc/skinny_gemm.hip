@@ -2,7 +2,7 @@
 // (code-1)*d, the ternary GEMM of "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs"
 // on the f16 MFMA path (same operands and bound as the tiled kernel).
 //
-// For M <= 16 the whole of x fits in LDS as f16, so a workgroup stages it once
+// For M <= 16 (M*K <= 65536) the whole of x fits in LDS as f16, so a workgroup stages it once
 // and its waves then run without barriers: each wave streams the code words of
 // the workgroup's 32 output columns over its own share of K (a half, quarter or
 // eighth) straight from HBM into registers, several steps ahead, decodes them and issues
@@ -206,8 +206,28 @@ hipError_t run_skinny(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
 
 bool skinny_fits(const DevWeight &w, int64_t M) {
     // eight waves of 64 k-wide steps: K % 512 == 0; x staged in one round of at
-    // most 16 pieces per thread: M*K/4 <= 512*16
-    return M >= 1 && M <= kSkinnyMaxM && w.K % 512 == 0 && M * w.K <= 4 * 512 * 16;
+    // most 32 pieces per thread (M*K/4 <= 512*32) and, as f16 with padded rows,
+    // within the LDS of a workgroup
+    if (M < 1 || M > kSkinnyMaxM || w.K % 512 != 0 || M * w.K > 4 * 512 * 32 ||
+        (size_t)M * (w.K + 8) * 2 > kSkinnyMaxLds)
+        return false;
+    // More than 16 pieces per thread only with 32-column workgroups (N <= 8192):
+    // measured with cold weights at K = 4096, M = 12..16, the skinny kernel takes
+    // 10.1-10.3 us against the tiled kernel's 13.1 at N = 4096, but 14.3 against
+    // 13.7-13.8 at N = 14336 (64-column workgroups, each staging all of x).
+    return M * w.K <= 4 * 512 * 16 || (w.N + 31) / 32 <= 256;
+}
+
+// Pieces of x per thread: 2, 16 or 32 (the fewest that cover M*K/4 over 512
+// threads); 32 only with one column block (skinny_fits).
+template <int NBW, int D>
+hipError_t run_skinny_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+    const int64_t per_thread = ((int64_t)a.M * a.K / 4 + 511) / 512;
+    if (per_thread <= 2) return run_skinny<NBW, 8, D, 2>(a, lds, dev, s);
+    if constexpr (NBW == 1) {
+        if (per_thread > 16) return run_skinny<1, 8, D, 32>(a, lds, dev, s);
+    }
+    return run_skinny<NBW, 8, D, 16>(a, lds, dev, s);
 }
 
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s) {
@@ -226,19 +246,18 @@ hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M
     const size_t xb = (size_t)M * (w.K + 8) * 2, rb = (size_t)7 * 16 * 64 * 4;
     const size_t lds = xb > rb ? xb : rb;
     const int64_t steps = w.K / 512;
-    const bool small = M * w.K <= 4 * 512 * 2;  // two pieces per thread suffice
     // one workgroup per CU: 64 columns per workgroup once 32-column ones would
     // outnumber the CUs
     if ((w.N + 31) / 32 > 256) {
         const size_t lds2 = xb > 2 * rb ? xb : 2 * rb;
-        if (steps % 4 == 0) return small ? run_skinny<2, 8, 4, 2>(a, lds2, dev, s) : run_skinny<2, 8, 4, 16>(a, lds2, dev, s);
-        if (steps % 2 == 0) return small ? run_skinny<2, 8, 2, 2>(a, lds2, dev, s) : run_skinny<2, 8, 2, 16>(a, lds2, dev, s);
-        return small ? run_skinny<2, 8, 1, 2>(a, lds2, dev, s) : run_skinny<2, 8, 1, 16>(a, lds2, dev, s);
+        if (steps % 4 == 0) return run_skinny_u<2, 4>(a, lds2, dev, s);
+        if (steps % 2 == 0) return run_skinny_u<2, 2>(a, lds2, dev, s);
+        return run_skinny_u<2, 1>(a, lds2, dev, s);
     }
-    if (steps % 8 == 0) return small ? run_skinny<1, 8, 8, 2>(a, lds, dev, s) : run_skinny<1, 8, 8, 16>(a, lds, dev, s);
-    if (steps % 4 == 0) return small ? run_skinny<1, 8, 4, 2>(a, lds, dev, s) : run_skinny<1, 8, 4, 16>(a, lds, dev, s);
-    if (steps % 2 == 0) return small ? run_skinny<1, 8, 2, 2>(a, lds, dev, s) : run_skinny<1, 8, 2, 16>(a, lds, dev, s);
-    return small ? run_skinny<1, 8, 1, 2>(a, lds, dev, s) : run_skinny<1, 8, 1, 16>(a, lds, dev, s);
+    if (steps % 8 == 0) return run_skinny_u<1, 8>(a, lds, dev, s);
+    if (steps % 4 == 0) return run_skinny_u<1, 4>(a, lds, dev, s);
+    if (steps % 2 == 0) return run_skinny_u<1, 2>(a, lds, dev, s);
+    return run_skinny_u<1, 1>(a, lds, dev, s);
 }
 
 }  // namespace tq2

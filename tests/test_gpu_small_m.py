@@ -1,7 +1,7 @@
 """GPU parity of the MFMA path's small-M kernels with the oracle.
 
-Up to 16 rows (with M*K <= 32768) the MFMA path runs the skinny kernel: x is
-staged whole in LDS and eight waves each take one eighth of K, their partial
+Up to 16 rows (with M*K <= 32768, or <= 65536 when N <= 8192) the MFMA path runs
+the skinny kernel: x is staged whole in LDS and eight waves each take one eighth of K, their partial
 tiles added in wave order.  Other M <= 32 take 32x64 tiles and 33 <= M <= 64
 take 64x64 tiles, whose waves split each step's K (four ways; with K/128 a
 multiple of 8, each of the four takes two 64-wide slices of a 512-wide step;
@@ -31,13 +31,13 @@ def torch():
 
 # K/128 = 32 (multiple of 8: four k groups of two slices), 12 (multiple of 4
 # only: four k groups), 6 (even: two k groups), 3 (odd: 256-column tiles).  Of
-# these only K=4096 and 1536 give K % 512 == 0, so M <= 16 (and M*K <= 32768)
-# runs the skinny kernel there and the tiled kernels otherwise.
+# these only K=4096 and 1536 give K % 512 == 0, so M <= 16 (and M*K <= 65536 at
+# this N) runs the skinny kernel there and the tiled kernels otherwise.
 KS = [4096, 1536, 768, 384]
 
 
 @pytest.mark.parametrize("k", KS)
-@pytest.mark.parametrize("m", [1, 5, 8, 16, 31, 32, 33, 64])
+@pytest.mark.parametrize("m", [1, 5, 8, 12, 16, 31, 32, 33, 64])
 def test_small_m_tiles_match_oracle(torch, m, k):
     n = 1000  # 16 column tiles, the last one partial
     aos = wl.sweep_weight(n, k)
