@@ -315,7 +315,45 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         }
     }
 
-    if constexpr (WK > 1) {
+    // Two k groups with an even share of blocks per round split the sums: each
+    // group owns half the accumulator blocks, hands the other half to its partner
+    // through LDS, adds what it receives and stores its own half, so both groups
+    // add and store.  Floating-point addition is commutative, so group 1's
+    // acc1 + acc0 has the bits of acc0 + acc1.
+    constexpr bool SPLIT = WK == 2 && (MB * NB) % (2 * RED_ROUNDS) == 0;
+    constexpr int HALF = MB * NB / 2;
+    if constexpr (SPLIT) {
+        constexpr int HPR = HALF / RED_ROUNDS;  // blocks each group hands over per round
+        float *red = reinterpret_cast<float *>(&As[0][0]);
+        auto at = [&](int g, int i, int r) { return ((g * NW + wr) * HPR + i) * 1024 + r * 64 + lane; };
+#pragma unroll
+        for (int ro = 0; ro < RED_ROUNDS; ++ro) {
+#pragma unroll
+            for (int i = 0; i < HPR; ++i) {
+                const int b0 = HALF + ro * HPR + i, b1 = ro * HPR + i;  // group 0 hands over b0, group 1 b1
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (wk == 0)
+                        red[at(0, i, r)] = acc[b0 / NB][b0 % NB][r];
+                    else
+                        red[at(1, i, r)] = acc[b1 / NB][b1 % NB][r];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < HPR; ++i) {
+                const int b0 = ro * HPR + i, b1 = HALF + ro * HPR + i;  // blocks each group owns
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (wk == 0)
+                        acc[b0 / NB][b0 % NB][r] += red[at(1, i, r)];
+                    else
+                        acc[b1 / NB][b1 % NB][r] += red[at(0, i, r)];
+                }
+            }
+            if (ro + 1 < RED_ROUNDS) __syncthreads();
+        }
+    } else if constexpr (WK > 1) {
         // k groups 1..WK-1 leave their partial tiles in LDS (over the A tiles,
         // which the loop no longer reads); group 0 adds them in group order.
         // When they do not fit at once, accumulator blocks go in rounds.
@@ -353,6 +391,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+            if (SPLIT && ((mb * NB + nb) < HALF) != (wk == 0)) continue;  // the partner group stores it
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
             if (gn >= p.N) continue;
             float rf = 1.0f;
