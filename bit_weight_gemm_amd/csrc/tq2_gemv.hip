@@ -9,6 +9,7 @@
 #include "internal.h"
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 namespace tq2 {
 
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
 // sum, so the same bits), with Q row quads per workgroup: waves 4q .. 4q+3
 // take row quad q.  Workgroups of eight waves (Q = 2) halve the workgroup count
 // at the same wave count; the cold 4096 x 4096 decode takes 3.97 us against
-// 4.09 with four-wave workgroups, and 3.78 us with the code words loaded
-// non-temporally.
+// 4.09 with four-wave workgroups, and 3.70-3.75 us with the code words and
+// scales loaded non-temporally.
 template <int Q>
 __global__ __launch_bounds__(256 * Q) void gemv_m1_kernel(const uint32_t *__restrict__ codes,
                                                           const uint16_t *__restrict__ scales,
@@ -194,9 +195,10 @@ __global__ __launch_bounds__(256 * Q) void gemv_m1_kernel(const uint32_t *__rest
         const int g = (kp >> 4) + kwave * 64 + lane;  // group index within the row
         if (g < kw) {
             // all loads of the pass before any arithmetic: one memory round trip; the
-            // code words are read once per call, so they are loaded non-temporally
+            // code words and scales are read once per call, so they are loaded
+            // non-temporally (x, which every workgroup reads, is not)
             const u4 cv = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(codes) + (int64_t)(n0 >> 2) * kw + g);
-            const uint2 sv = reinterpret_cast<const uint2 *>(scales)[(int64_t)(n0 >> 2) * kb + (g >> 3)];
+            const u2 sv = __builtin_nontemporal_load(reinterpret_cast<const u2 *>(scales) + (int64_t)(n0 >> 2) * kb + (g >> 3));
             const f4 *xp = reinterpret_cast<const f4 *>(x + g * 16);
             f4 xr[4];
 #pragma unroll
