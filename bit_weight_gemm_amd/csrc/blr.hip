@@ -60,78 +60,113 @@ BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 
 // Sign bitmaps -> code words (set bit -> code 2 = +1, clear -> code 0 = -1,
 // padding -> code 1 = 0) in the device layout, with row index n and
-// contraction index k, for both matrices in one launch.  A thread makes the
-// 16-byte unit of four rows (4q .. 4q+3) for one 16-wide k group g.
-//   S_V: sign(n, k) = bit n of bits_v[k][n/32]   (n = rank, k = input j): a wave
-//        takes 64 consecutive row quads of one group, so each of its 16 loads
-//        (one per k) touches 8 bitmap words shared by the lanes;
-//   S_U: sign(n, k) = bit k of bits_u[n][k/32]   (n = output i, k = rank): the
-//        threads walk (row quad, group) with the group fastest, so a wave's
-//        loads read whole bitmap rows and its stores are contiguous.
+// contraction index k.  A thread makes the 16-byte unit of four rows
+// (4q .. 4q+3) for one 16-wide k group g.  Two orientations of the bitmap:
+//   kRowBits: sign(n, k) = bit n of bits[k][n/32] (rows n are the rank: S_V in
+//             the forward, S_U^T in the backward): a wave takes 64 consecutive
+//             row quads of one group, so each of its 16 loads (one per k)
+//             touches 8 bitmap words shared by the lanes;
+//   kKBits:   sign(n, k) = bit k of bits[n][k/32] (the contraction is the rank:
+//             S_U in the forward, S_V in the backward): the threads walk (row
+//             quad, group) with the group fastest, so a wave's loads read whole
+//             bitmap rows and its stores are contiguous.
 // Out-of-range elements read a valid word and are replaced by code 1.
-// Blocks from nblk_v + nblk_u on write xg[m][k] = f16(x[m][k] * g[k]) (product in
-// f32, round to nearest even) for k < d_in and 0 up to kpad1, 8 values per thread.
+enum RelayKind { kRowBits = 0, kKBits = 1 };
+struct RelayJob {
+    const uint32_t *bits;
+    uint32_t *codes;
+    int64_t nvalid, kvalid;  // rows and contraction indices present (the rank is one of them)
+    int64_t npad, kpad;      // padded rows and contraction of the code plane
+    int64_t nblk;            // workgroups of the launch this job takes
+    int kind;
+};
+
+static RelayJob relay_job(int kind, const uint32_t *bits, uint32_t *codes, int64_t nvalid, int64_t kvalid,
+                          int64_t npad, int64_t kpad) {
+    RelayJob j{};
+    j.bits = bits, j.codes = codes, j.nvalid = nvalid, j.kvalid = kvalid, j.npad = npad, j.kpad = kpad, j.kind = kind;
+    j.nblk = kind == kRowBits ? ((npad / 4 + 255) / 256) * (kpad / 16) : ((npad / 4) * (kpad / 16) + 255) / 256;
+    return j;
+}
+
+// One launch: the re-layout jobs in order, then (blocks after them) xg[m][k] =
+// f16(x[m][k] * g[k]) (product in f32, round to nearest even) for k < d_in and 0
+// up to kpad1, 8 values per thread.
+constexpr int kMaxRelayJobs = 4;
 struct BlrPrep {
-    const uint32_t *bits_v, *bits_u;
-    uint32_t *codes_v, *codes_u;
+    RelayJob job[kMaxRelayJobs];
+    int njobs;
+    int64_t words;                     // r / 32
     const float *x, *g;
     _Float16 *xg;
-    int64_t words;                     // r / 32
-    int64_t M, r, d_in, d_out;
-    int64_t npad1, kpad1, npad2, kpad2;
-    int64_t nblk_v, nblk_u;
+    int64_t M, d_in, kpad1;
     int xvec;                          // x rows and g allow 16-byte loads
 };
 
 // code of element e (0..15) at its place in a group word
 __device__ __forceinline__ uint32_t code_at(uint32_t code, int e) { return code << (2 * (e >> 1) + 16 * (e & 1)); }
 
-__global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
-    const int64_t bid = blockIdx.x;
-    if (bid < q.nblk_v) {
-        const int64_t kw = q.kpad1 / 16, quads = q.npad1 / 4;
-        const int64_t qblocks = (quads + 255) / 256;
-        const int64_t quad = (bid % qblocks) * 256 + threadIdx.x, g = bid / qblocks;
-        if (quad >= quads) return;
-        const int64_t n0 = quad * 4;
-        const bool nin = n0 < q.r;  // r % 32 == 0: a quad is wholly inside or wholly past r
-        const int64_t wrd = nin ? n0 >> 5 : 0;
-        const int sh = (int)(n0 & 31);
-        u4 out = {0, 0, 0, 0};
+__device__ __forceinline__ void relay_row_bits(const RelayJob &j, int64_t words, int64_t bid) {
+    const int64_t kw = j.kpad / 16, quads = j.npad / 4;
+    const int64_t qblocks = (quads + 255) / 256;
+    const int64_t quad = (bid % qblocks) * 256 + threadIdx.x, g = bid / qblocks;
+    if (quad >= quads) return;
+    const int64_t n0 = quad * 4;
+    const bool nin = n0 < j.nvalid;  // the rank is a multiple of 32: a quad is wholly inside or past it
+    const int64_t wrd = nin ? n0 >> 5 : 0;
+    const int sh = (int)(n0 & 31);
+    u4 out = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int64_t k = g * 16 + e;
+        const bool in = nin && k < j.kvalid;
+        const uint32_t bits = (j.bits[(in ? k : 0) * words + wrd] >> sh) & 15u;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) out[rr] |= code_at(in ? (((bits >> rr) & 1u) ? 2u : 0u) : 1u, e);
+    }
+    *reinterpret_cast<u4 *>(j.codes + (quad * kw + g) * 4) = out;
+}
+
+__device__ __forceinline__ void relay_k_bits(const RelayJob &j, int64_t words, int64_t bid) {
+    const int64_t kw = j.kpad / 16;
+    const int64_t item = bid * 256 + threadIdx.x;
+    if (item >= (j.npad / 4) * kw) return;
+    const int64_t quad = item / kw, g = item % kw;
+    u4 out;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int64_t n = quad * 4 + rr;
+        const bool in = n < j.nvalid && g * 16 < j.kvalid;
+        const uint32_t half = (j.bits[(in ? n : 0) * words + (in ? g >> 1 : 0)] >> (16 * (g & 1))) & 0xFFFFu;
+        uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int64_t k = g * 16 + e;
-            const bool in = nin && k < q.d_in;
-            const uint32_t bits = (q.bits_v[(in ? k : 0) * q.words + wrd] >> sh) & 15u;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                out[rr] |= code_at(in ? (((bits >> rr) & 1u) ? 2u : 0u) : 1u, e);
+            const bool ine = in && g * 16 + e < j.kvalid;
+            w |= code_at(ine ? (((half >> e) & 1u) ? 2u : 0u) : 1u, e);
         }
-        *reinterpret_cast<u4 *>(q.codes_v + (quad * kw + g) * 4) = out;
-    } else if (bid < q.nblk_v + q.nblk_u) {
-        const int64_t kw = q.kpad2 / 16;
-        const int64_t item = (bid - q.nblk_v) * 256 + threadIdx.x;
-        if (item >= (q.npad2 / 4) * kw) return;
-        const int64_t quad = item / kw, g = item % kw;
-        u4 out;
+        out[rr] = w;
+    }
+    *reinterpret_cast<u4 *>(j.codes + (quad * kw + g) * 4) = out;
+}
+
+__global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
+    int64_t bid = blockIdx.x;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int64_t n = quad * 4 + rr;
-            const bool in = n < q.d_out && g * 16 < q.r;
-            const uint32_t half = (q.bits_u[(in ? n : 0) * q.words + (in ? g >> 1 : 0)] >> (16 * (g & 1))) & 0xFFFFu;
-            uint32_t w = 0;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const bool ine = in && g * 16 + e < q.r;
-                w |= code_at(ine ? (((half >> e) & 1u) ? 2u : 0u) : 1u, e);
-            }
-            out[rr] = w;
+    for (int jb = 0; jb < kMaxRelayJobs; ++jb) {
+        if (jb >= q.njobs) break;
+        if (bid < q.job[jb].nblk) {
+            if (q.job[jb].kind == kRowBits)
+                relay_row_bits(q.job[jb], q.words, bid);
+            else
+                relay_k_bits(q.job[jb], q.words, bid);
+            return;
         }
-        *reinterpret_cast<u4 *>(q.codes_u + (quad * kw + g) * 4) = out;
-    } else {
+        bid -= q.job[jb].nblk;
+    }
+    {
         typedef _Float16 h8 __attribute__((ext_vector_type(8)));
         const int64_t per_row = q.kpad1 / 8;
-        const int64_t piece = (bid - q.nblk_v - q.nblk_u) * 256 + threadIdx.x;
+        const int64_t piece = bid * 256 + threadIdx.x;
         if (piece >= q.M * per_row) return;
         const int64_t m = piece / per_row, k0 = (piece % per_row) * 8;
         const float *xr = q.x + m * q.d_in;
@@ -153,6 +188,28 @@ __global__ __launch_bounds__(256) void blr_prep_kernel(BlrPrep q) {
     }
 }
 
+// The forward's preparation: both bitmaps re-laid and f16(x.g), one launch.
+static BlrPrep forward_prep(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v, uint32_t *codes_u,
+                            uint32_t *codes_v, const float *x, const float *g, _Float16 *xg) {
+    BlrPrep q{};
+    q.job[0] = relay_job(kRowBits, bits_v, codes_v, pl.r, pl.d_in, pl.npad1, pl.kpad1);   // S_V
+    q.job[1] = relay_job(kKBits, bits_u, codes_u, pl.d_out, pl.r, pl.npad2, pl.kpad2);    // S_U
+    q.njobs = 2;
+    q.words = pl.r / 32;
+    q.x = x, q.g = g, q.xg = xg, q.M = pl.M, q.d_in = pl.d_in, q.kpad1 = pl.kpad1;
+    q.xvec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+             ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+    return q;
+}
+
+static hipError_t run_prep(const BlrPrep &q, hipStream_t s) {
+    int64_t blocks = (q.M * (q.kpad1 / 8) + 255) / 256;
+    for (int j = 0; j < q.njobs; ++j) blocks += q.job[j].nblk;
+    if (blocks < 1) return hipSuccess;
+    blr_prep_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(q);
+    return hipGetLastError();
+}
+
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
                               void *workspace, bool accumulate, hipStream_t s) {
@@ -162,18 +219,7 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
     _Float16 *al = reinterpret_cast<_Float16 *>(ws + pl.off_al);
     _Float16 *xg = reinterpret_cast<_Float16 *>(ws + pl.off_xg);
     {
-        BlrPrep q{};
-        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
-        q.x = x, q.g = g, q.xg = xg;
-        q.words = pl.r / 32, q.M = pl.M, q.r = pl.r, q.d_in = pl.d_in, q.d_out = pl.d_out;
-        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
-        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
-        q.nblk_u = ((pl.npad2 / 4) * (pl.kpad2 / 16) + 255) / 256;
-        q.xvec = (pl.d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
-        const int64_t nblk_x = (pl.M * (pl.kpad1 / 8) + 255) / 256;
-        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
-        hipError_t e = hipGetLastError();
+        hipError_t e = run_prep(forward_prep(pl, bits_u, bits_v, codes_u, codes_v, x, g, xg), s);
         if (e != hipSuccess) return e;
     }
     // GEMM1: al[M][kpad2] = f16(l . (xg . S_V)); rows of S_V past r are code 1, so
@@ -343,31 +389,15 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     float *dxp = reinterpret_cast<float *>(at(pb.off_dxp));
     float *part = reinterpret_cast<float *>(at(pb.off_part));
     hipError_t e;
-    // bitmaps in both orientations, and f16(x.g)
+    // bitmaps in both orientations and f16(x.g), one launch
     {
-        BlrPrep q{};
-        q.bits_v = bits_v, q.bits_u = bits_u, q.codes_v = codes_v, q.codes_u = codes_u;
-        q.x = x, q.g = g, q.xg = xg;
-        q.words = r / 32, q.M = M, q.r = r, q.d_in = d_in, q.d_out = d_out;
-        q.npad1 = pl.npad1, q.kpad1 = pl.kpad1, q.npad2 = pl.npad2, q.kpad2 = pl.kpad2;
-        q.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pl.kpad1 / 16);
-        q.nblk_u = ((pl.npad2 / 4) * (pl.kpad2 / 16) + 255) / 256;
-        q.xvec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                 ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
-        const int64_t nblk_x = (M * (pl.kpad1 / 8) + 255) / 256;
-        blr_prep_kernel<<<dim3((unsigned)(q.nblk_v + q.nblk_u + nblk_x)), dim3(256), 0, s>>>(q);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        BlrPrep q = forward_prep(pl, bits_u, bits_v, codes_u, codes_v, x, g, xg);
         // S_U^T: rows r, contraction d_out (bits along the rows, as S_V's);
         // S_V: rows d_in, contraction r (bits along the contraction, as S_U's)
-        BlrPrep t{};
-        t.bits_v = bits_u, t.codes_v = codes_ut, t.d_in = d_out, t.kpad1 = pb.kpado, t.npad1 = pl.npad1;
-        t.bits_u = bits_v, t.codes_u = codes_vt, t.d_out = d_in, t.kpad2 = pl.kpad2, t.npad2 = pb.npadi;
-        t.words = r / 32, t.M = 0, t.r = r;
-        t.nblk_v = ((pl.npad1 / 4 + 255) / 256) * (pb.kpado / 16);
-        t.nblk_u = ((pb.npadi / 4) * (pl.kpad2 / 16) + 255) / 256;
-        blr_prep_kernel<<<dim3((unsigned)(t.nblk_v + t.nblk_u)), dim3(256), 0, s>>>(t);
-        e = hipGetLastError();
+        q.job[2] = relay_job(kRowBits, bits_u, codes_ut, r, d_out, pl.npad1, pb.kpado);
+        q.job[3] = relay_job(kKBits, bits_v, codes_vt, d_in, r, pb.npadi, pl.kpad2);
+        q.njobs = 4;
+        e = run_prep(q, s);
         if (e != hipSuccess) return e;
     }
     const bool small = blr_small_tiles(M, pl.kpad2);
