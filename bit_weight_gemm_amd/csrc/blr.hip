@@ -266,7 +266,6 @@ BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     p.kpado = round_up(d_out, kBlrKPad);
     p.npadi = round_up(d_in, kRowPad);
     p.chunks = (M + kColChunk - 1) / kColChunk;
-    const int64_t widest = d_in > d_out ? (d_in > r ? d_in : r) : (d_out > r ? d_out : r);
     size_t off = p.fwd.total;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -281,7 +280,10 @@ BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     p.off_db = take((size_t)M * r * 4);
     p.off_dbl = take((size_t)M * p.fwd.kpad2 * 2);
     p.off_dxp = take((size_t)M * d_in * 4);
-    p.off_part = take((size_t)(p.chunks > 0 ? p.chunks : 1) * widest * 4);
+    const size_t ch = (size_t)(p.chunks > 0 ? p.chunks : 1);
+    p.off_part_dh = take(ch * d_out * 4);
+    p.off_part_dl = take(ch * r * 4);
+    p.off_part_dg = take(ch * d_in * 4);
     p.total = off;
     return p;
 }
@@ -290,12 +292,33 @@ namespace {
 
 enum ColMode { kColStageH = 0, kColDx = 1, kColDxAcc = 2 };
 
+// Pass 2 of a column sum, for column n: out[n] = f32(out[n] + f32(sum over chunks
+// in order of part[ch][n])).  The loads of a group of chunks are independent:
+// issue them together, then add in order.
+__device__ __forceinline__ void column_finish(const float *__restrict__ part, float *__restrict__ out, int64_t N,
+                                              int64_t chunks, int64_t n) {
+    float s = 0.0f;
+    int64_t ch = 0;
+    for (; ch + 16 <= chunks; ch += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = part[(ch + i) * N + n];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += v[i];
+    }
+    for (; ch < chunks; ++ch) s += part[ch * N + n];
+    out[n] = out[n] + s;
+}
+
 // Pass 1 of a column sum: part[ch][n] = sum over tokens t of chunk ch of
 // A[t][n] * B[t][n] (f32, ascending t), for n < N.  Fused with the elementwise
 // op that reads the same operand A:
 //   kColStageH: H[t][n] = f16(A[t][n] * f[n] * gs) for n < N, 0 for N <= n < ldh;
 //   kColDx:     D[t][n] = f[n] * B[t][n];
 //   kColDxAcc:  D[t][n] = f32(D[t][n] + f32(f[n] * B[t][n])).
+// Workgroups past the column blocks (chunk 0 only) run pass 2 of an earlier
+// column sum (fpart -> fout, fN columns, fchunks chunks), which saves it a launch
+// of its own; its partials are in a buffer of their own, so the two do not meet.
 struct ColArgs {
     const float *A, *B, *f;
     float *part;
@@ -303,15 +326,24 @@ struct ColArgs {
     float *D;
     int64_t M, N, lda, ldh;
     float gs;
+    const float *fpart;  // earlier column sum to finish, or nullptr
+    float *fout;
+    int64_t fN, fchunks;
 };
 
 template <int MODE>
 __global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
 #pragma clang fp contract(off)
+    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
+    const int64_t cblocks = (ncols + 255) / 256;
+    if ((int64_t)blockIdx.x >= cblocks) {
+        const int64_t n = ((int64_t)blockIdx.x - cblocks) * 256 + threadIdx.x;
+        if (blockIdx.y == 0 && n < q.fN) column_finish(q.fpart, q.fout, q.fN, q.fchunks, n);
+        return;
+    }
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t ch = blockIdx.y;
     const int64_t t0 = ch * kColChunk, t1 = t0 + kColChunk < q.M ? t0 + kColChunk : q.M;
-    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
     if (n >= ncols) return;
     if (n >= q.N) {  // padding columns of the staged operand
         for (int64_t t = t0; t < t1; ++t) q.H[t * q.ldh + n] = (_Float16)0.0f;
@@ -337,32 +369,19 @@ __global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
     q.part[ch * q.N + n] = sum;
 }
 
-// Pass 2: out[n] = f32(out[n] + f32(sum over chunks in order of part[ch][n])).
+// Pass 2 alone (the last column sum of a path).
 __global__ __launch_bounds__(256) void blr_colsum_finish_kernel(const float *__restrict__ part, float *__restrict__ out,
                                                                 int64_t N, int64_t chunks) {
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    // the loads of a group of chunks are independent: issue them together, then add in order
-    float s = 0.0f;
-    int64_t ch = 0;
-    for (; ch + 16 <= chunks; ch += 16) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = part[(ch + i) * N + n];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += v[i];
-    }
-    for (; ch < chunks; ++ch) s += part[ch * N + n];
-    out[n] = out[n] + s;
+    if (n < N) column_finish(part, out, N, chunks, n);
 }
 
+// Pass 1 of q (and pass 2 of the column sum q.fpart names, if any).
 template <int MODE>
-hipError_t colsum(const ColArgs &q, float *out, int64_t chunks, hipStream_t s) {
+hipError_t colsum_pass1(const ColArgs &q, int64_t chunks, hipStream_t s) {
     const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
-    blr_colsum_kernel<MODE><<<dim3((unsigned)((ncols + 255) / 256), (unsigned)chunks), dim3(256), 0, s>>>(q);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    blr_colsum_finish_kernel<<<dim3((unsigned)((q.N + 255) / 256)), dim3(256), 0, s>>>(q.part, out, q.N, chunks);
+    const int64_t fblocks = q.fpart ? (q.fN + 255) / 256 : 0;
+    blr_colsum_kernel<MODE><<<dim3((unsigned)((ncols + 255) / 256 + fblocks), (unsigned)chunks), dim3(256), 0, s>>>(q);
     return hipGetLastError();
 }
 
@@ -387,7 +406,9 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     float *db = reinterpret_cast<float *>(at(pb.off_db));
     _Float16 *dbl = reinterpret_cast<_Float16 *>(at(pb.off_dbl));
     float *dxp = reinterpret_cast<float *>(at(pb.off_dxp));
-    float *part = reinterpret_cast<float *>(at(pb.off_part));
+    float *part_dh = reinterpret_cast<float *>(at(pb.off_part_dh));
+    float *part_dl = reinterpret_cast<float *>(at(pb.off_part_dl));
+    float *part_dg = reinterpret_cast<float *>(at(pb.off_part_dg));
     hipError_t e;
     // bitmaps in both orientations and f16(x.g), one launch
     {
@@ -421,9 +442,9 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     // dh += sum_t dy.c, with dyh = f16(dy.h.gs) staged from the same reads
     {
         ColArgs q{};
-        q.A = dy, q.B = c, q.f = h, q.part = part, q.H = dyh, q.M = M, q.N = d_out, q.lda = d_out, q.ldh = pb.kpado;
+        q.A = dy, q.B = c, q.f = h, q.part = part_dh, q.H = dyh, q.M = M, q.N = d_out, q.lda = d_out, q.ldh = pb.kpado;
         q.gs = gs;
-        e = colsum<kColStageH>(q, dh, pb.chunks, s);
+        e = colsum_pass1<kColStageH>(q, pb.chunks, s);
         if (e != hipSuccess) return e;
     }
     // db = dyh . S_U / gs   [M][r]
@@ -438,9 +459,10 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     // dl += sum_t a.db, with dbl = f16(db.l.gs) staged from the same reads
     {
         ColArgs q{};
-        q.A = db, q.B = a, q.f = l, q.part = part, q.H = dbl, q.M = M, q.N = r, q.lda = r, q.ldh = pl.kpad2;
+        q.A = db, q.B = a, q.f = l, q.part = part_dl, q.H = dbl, q.M = M, q.N = r, q.lda = r, q.ldh = pl.kpad2;
         q.gs = gs;
-        e = colsum<kColStageH>(q, dl, pb.chunks, s);
+        q.fpart = part_dh, q.fout = dh, q.fN = d_out, q.fchunks = pb.chunks;  // and dh's second pass
+        e = colsum_pass1<kColStageH>(q, pb.chunks, s);
         if (e != hipSuccess) return e;
     }
     // dx' = dbl . S_V^T / gs   [M][d_in]
@@ -455,8 +477,12 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
     {
         ColArgs q{};
-        q.A = x, q.B = dxp, q.f = g, q.part = part, q.D = dx, q.M = M, q.N = d_in, q.lda = d_in;
-        e = accumulate_dx ? colsum<kColDxAcc>(q, dg, pb.chunks, s) : colsum<kColDx>(q, dg, pb.chunks, s);
+        q.A = x, q.B = dxp, q.f = g, q.part = part_dg, q.D = dx, q.M = M, q.N = d_in, q.lda = d_in;
+        q.fpart = part_dl, q.fout = dl, q.fN = r, q.fchunks = pb.chunks;  // and dl's second pass
+        e = accumulate_dx ? colsum_pass1<kColDxAcc>(q, pb.chunks, s) : colsum_pass1<kColDx>(q, pb.chunks, s);
+        if (e != hipSuccess) return e;
+        blr_colsum_finish_kernel<<<dim3((unsigned)((d_in + 255) / 256)), dim3(256), 0, s>>>(part_dg, dg, d_in, pb.chunks);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
