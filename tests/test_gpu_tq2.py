@@ -180,6 +180,27 @@ def test_odd_widths(torch, n, k, path):
         w.close()
 
 
+@pytest.mark.parametrize("n,k", [(600, 768), (600, 640)])
+def test_large_m_tile_boundaries(torch, n, k):
+    """M just past the small-M kernels and around the 96- and 128-row tiles the MFMA
+    path picks for M > 64 (rows past M read row M-1 and are not stored), N = 600
+    (a ragged third column tile), K/128 = 6 (two k groups splitting the partial-tile
+    sums) and 5 (one k group); full comparison with the oracle and a bitwise repeat."""
+    aos = wl.sweep_weight(n, k)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for m in (65, 95, 96, 97, 127, 128, 129, 191, 192, 193):
+            x = wl.sweep_x(m, k)
+            note(f"[large-M tiles] M={m} N={n} K={k}")
+            y = run_tq2(w, x, "mfma")
+            y64, b = oracle.gemm(aos, n, k, x)
+            assert_within(y, y64, b, MFMA_REL, f"large-M tiles M={m} N={n} K={k}")
+            again = run_tq2(w, x, "mfma")
+            assert np.array_equal(y.view(np.uint32), again.view(np.uint32)), f"not deterministic at M={m}"
+    finally:
+        w.close()
+
+
 @pytest.mark.parametrize("path", ["f32", "mfma"])
 def test_many_rows(torch, path):
     """M = 300000 rows: the f32 path's grid runs in slices of 65535 row tiles, and the
