@@ -37,7 +37,7 @@ __device__ __forceinline__ int xs_row(int r, int K) { return r * (K + 8); }
 
 // NBW: 32-column blocks per wave (and per workgroup); WK: waves, each owning
 // K/WK of the contraction; D: steps of 64 k whose code words are in flight;
-// U: pieces of x (4 values) each thread stages, with WK*64*U >= M*K/4.
+// U: pieces of x (4 values) each lane stages, with 64*U >= M*K/(4*WK).
 template <int NBW, int WK, int D, int U>
 __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -72,32 +72,34 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
             dv[slot][nb] = p.scales[sbase[nb] + 4 * (tc >> 1)];
         }
     };
-    // ---- stage x once: f32 -> f16 (round to nearest even), 4 values per piece;
-    // a thread stages U pieces of [M][K/4] (row-major), T apart, and T*U covers
-    // all of x.  The loads go out before the weight stream starts and the LDS
-    // stores wait only for them (the memory counter retires in issue order), so
-    // x comes from L2 while the first code words are still on their way from
-    // HBM.  Slots past the end re-read the thread's first piece and store
-    // nothing, which keeps the loads free of branches.
-    const int per_row = p.K / 4;
-    const int total = p.M * per_row;
+    // ---- stage x once: f32 -> f16 (round to nearest even), 4 values per piece.
+    // Each wave stages the slice it reads, all M rows of its K range [kbeg,
+    // kbeg + K/WK): M*qw pieces with qw = K/(4*WK) per row, lane l taking
+    // U of them, 64 apart.  No wave reads another's slice, so the loop needs no
+    // workgroup barrier, only the wave's own LDS stores, and each wave starts as
+    // soon as its own x and code words are in.  The loads go out before the
+    // weight stream starts and the LDS stores wait only for them (the memory
+    // counter retires in issue order), so x comes from L2 while the first code
+    // words are still on their way from HBM.  Slots past the end re-read the
+    // lane's first piece and store nothing, which keeps the loads free of
+    // branches.
+    const int qw = kw_wave / 4;  // pieces per row of the slice (>= 16)
+    const int total = p.M * qw;
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    constexpr int T = WK * 64;
-    const int adv_r = T / per_row, adv_q = T % per_row;  // (row, q) advance per T pieces
     f4 xv[U];
-    // Each workgroup walks x from its own starting piece (wrapping at the end),
-    // so the workgroups on one XCD do not all ask the same L2 channel for the
-    // same line at once.  Piece u of this thread is (start + tid + u*T) mod
-    // M*K/4, tracked as (row, q) and advanced without divisions.
+    // Each workgroup walks its slices from its own starting piece (wrapping at
+    // the end), so the workgroups on one XCD do not all ask the same L2 channel
+    // for the same line at once.  Piece u of this lane is (start + lane + 64u)
+    // mod M*qw, tracked as (row, q) and advanced without divisions.
     const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
-    const int s0 = (tid + start) % total;
-    const int r0 = s0 / per_row, q0 = s0 % per_row;
-    const int adv_rm = adv_r % p.M;
+    const int s0 = (lane + start) % total;
+    const int r0 = s0 / qw, q0 = s0 % qw;
+    const int adv_r = (64 / qw) % p.M, adv_q = 64 % qw;
     auto next = [&](int &r, int &q) {
         q += adv_q;
-        r += adv_rm;
-        if (q >= per_row) {
-            q -= per_row;
+        r += adv_r;
+        if (q >= qw) {
+            q -= qw;
             ++r;
         }
         if (r >= p.M) r -= p.M;
@@ -106,8 +108,8 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
         int r = r0, q = q0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool live = u * T + tid < total;
-            xv[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + 4 * (live ? q : q0));
+            const bool live = u * 64 + lane < total;
+            xv[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + kbeg + 4 * (live ? q : q0));
             next(r, q);
         }
     }
@@ -119,9 +121,9 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
         int r = r0, q = q0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (u * T + tid < total) {
+            if (u * 64 + lane < total) {
                 const h4 h = {(_Float16)xv[u][0], (_Float16)xv[u][1], (_Float16)xv[u][2], (_Float16)xv[u][3]};
-                *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + 4 * q]) = h;
+                *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 4 * q]) = h;
             }
             next(r, q);
         }
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
     for (int nb = 0; nb < NBW; ++nb) acc[nb] = f16x{};
     const int arow = lrow < p.M ? lrow : p.M - 1;  // rows past M repeat row M-1; never stored
 
-    // x is in LDS once every wave's stores are done; a plain barrier, so the
-    // code words in flight are not waited for here
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the wave's own slice is in LDS once its stores are done (no barrier: the
+    // code words in flight are not waited for here)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     for (int t0 = 0; t0 < nsteps; t0 += D) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
