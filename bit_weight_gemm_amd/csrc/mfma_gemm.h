@@ -92,7 +92,7 @@ __device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15);
 // AMODE: how A tiles are read.  kAExact: f32, K is a multiple of the step and
 // rows past M read row M-1 (ternary GEMM).  kABuf: as kAExact, but through a
 // buffer resource spanning the M rows, so loads of rows past M return zero
-// without a memory request (small M, M*lda*4 < 2^31).  kAHalf: A already
+// without a memory request ((rows of the last tile)*lda*4 < 2^31).  kAHalf: A already
 // rounded to f16, K a multiple of the step (zero-padded by the producer), rows
 // past M read row M-1.  Rows past M only reach output rows that are never stored.
 enum AMode { kAExact = 0, kABuf = 3, kAHalf = 4 };

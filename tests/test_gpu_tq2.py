@@ -201,6 +201,17 @@ def test_large_m_tile_boundaries(torch, n, k):
         w.close()
 
 
+def test_x_beyond_2gb_uses_64bit_addresses(torch):
+    """x of more than 2 GB (130944 x 4096 f32): the large-M tiles read it with 64-bit
+    addresses instead of the 32-bit buffer offsets used below 2 GB; sampled outputs
+    across the whole range of rows against the oracle."""
+    n, k, m = 64, 4096, 130944
+    assert (m + 256) * k * 4 >= 2 ** 31
+    aos = wl.sweep_weight(n, k)
+    x = wl.sweep_x(m, k)
+    check_tq2_sampled(aos, n, k, x, "mfma", "x beyond 2 GB", count=2048)
+
+
 @pytest.mark.parametrize("path", ["f32", "mfma"])
 def test_many_rows(torch, path):
     """M = 300000 rows: the f32 path's grid runs in slices of 65535 row tiles, and the
