@@ -77,9 +77,8 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     // step (two LDS buffers, one A register stage).  y (32 MB at M=2048,
     // N=4096) is stored non-temporally.  Where the tile count fills the rounds
     // of workgroups better, 96 x 256 tiles (two A register stages fit).  x is
-    // read through a buffer resource (32-bit offsets: fewer address registers
-    // and instructions than 64-bit addresses; 80 -> 76 us at 2048 x 4096 x 4096)
-    // while it and the rows of the last tile lie within 2 GB.
+    // read through a buffer resource (32-bit offsets: 10 fewer registers than
+    // 64-bit addresses) while it and the rows of the last tile lie within 2 GB.
     if (kb % 2 == 0) {
         const bool abuf = (M + 256) * w.K * 4 < ((int64_t)1 << 31);
         if (rows96(M, w.N, device_cus()))
