@@ -45,7 +45,7 @@ def tq2_bytes(n, k):
 
 
 KERNEL_SOURCES = {  # files whose content defines each timed kernel
-    "gemv_m1_kernel": ["tq2_gemv.hip", "decode.h", "internal.h"],
+    "gemv_mt_kernel": ["tq2_gemv.hip", "decode.h", "internal.h"],
     "mfma_gemm_kernel": ["mfma_gemm.h", "mfma_gemm.hip", "decode.h", "internal.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
@@ -495,8 +495,8 @@ def main():
                           f"HIP events on the launch stream")
         line["roofline"] = {"bound": "hbm", "achieved": round(d["gbs_step"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["gbs_step"] / HBM_PEAK_GBS, 4),
-                            "traffic": read_traffic("gemv_m1_kernel", "gemv_m1_decode_M1_traffic.txt"),
-                            "kernel": "gemv_m1_kernel", "kernel_us": round(d["step_ms"] * 1e3, 3)}
+                            "traffic": read_traffic("gemv_mt_kernel", "gemv_mt_decode_M1_traffic.txt"),
+                            "kernel": "gemv_mt_kernel", "kernel_us": round(d["step_ms"] * 1e3, 3)}
         line["eager_value"] = round(d["gbs_eager"], 2)
     if "prefill" in out:
         p = out["prefill"]

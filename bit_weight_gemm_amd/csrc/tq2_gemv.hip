@@ -167,22 +167,23 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
     }
 }
 
-// ------------------------------------------------------------------ M = 1 (decode)
+// ------------------------------------------------------------------ 1 <= M <= 4 (decode)
 //
-// The same per-lane work as gemv_f32_kernel<4, 1> (one 16-element group of four
+// The same per-lane work as gemv_f32_kernel<4, MT> (one 16-element group of four
 // weight rows per lane and 4096-wide pass, the same f16-pair decode, fused
 // multiply-adds, block scale, lane-sum exchanges and wave order of the final
-// sum, so the same bits), with Q row quads per workgroup: waves 4q .. 4q+3
-// take row quad q.  Workgroups of eight waves (Q = 2) halve the workgroup count
-// at the same wave count; the cold 4096 x 4096 decode takes 3.97 us against
-// 4.09 with four-wave workgroups, and 3.70-3.75 us with the code words and
-// scales loaded non-temporally.
-template <int Q>
-__global__ __launch_bounds__(256 * Q) void gemv_m1_kernel(const uint32_t *__restrict__ codes,
+// sum, so the same bits), for all MT = M <= 4 activation rows at once, with
+// Q row quads per workgroup: waves 4q .. 4q+3 take row quad q.  Workgroups of
+// eight waves (Q = 2) halve the workgroup count at the same wave count; the cold
+// 4096 x 4096 decode takes 3.97 us against 4.09 with four-wave workgroups, and
+// 3.70-3.75 us with the code words and scales, which one call reads once, loaded
+// non-temporally.
+template <int Q, int MT>
+__global__ __launch_bounds__(256 * Q) void gemv_mt_kernel(const uint32_t *__restrict__ codes,
                                                           const uint16_t *__restrict__ scales,
                                                           const float *__restrict__ x, float *__restrict__ y, int N,
                                                           int K) {
-    __shared__ float red[4 * Q][4];
+    __shared__ float red[4 * Q][4][MT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int quad = wave >> 2, kwave = wave & 3;
     const int row0 = blockIdx.x * 4 * Q;  // first weight row of the workgroup
@@ -190,7 +191,11 @@ __global__ __launch_bounds__(256 * Q) void gemv_m1_kernel(const uint32_t *__rest
     const int kw = K >> 4, kb = K / kBlock;
     const uint32_t magic = f16_magic();
 
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[4][MT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
     for (int kp = 0; kp < K; kp += 4096) {
         const int g = (kp >> 4) + kwave * 64 + lane;  // group index within the row
         if (g < kw) {
@@ -199,52 +204,66 @@ __global__ __launch_bounds__(256 * Q) void gemv_m1_kernel(const uint32_t *__rest
             // non-temporally (x, which every workgroup reads, is not)
             const u4 cv = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(codes) + (int64_t)(n0 >> 2) * kw + g);
             const u2 sv = __builtin_nontemporal_load(reinterpret_cast<const u2 *>(scales) + (int64_t)(n0 >> 2) * kb + (g >> 3));
-            const f4 *xp = reinterpret_cast<const f4 *>(x + g * 16);
-            f4 xr[4];
+            f4 xr[MT][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xr[i] = xp[i];
+            for (int t = 0; t < MT; ++t) {
+                const f4 *xp = reinterpret_cast<const f4 *>(x + (int64_t)t * K + g * 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xr[t][i] = xp[i];
+            }
             __builtin_amdgcn_sched_barrier(0);
             const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
             const uint16_t db[4] = {(uint16_t)(sv.x & 0xFFFFu), (uint16_t)(sv.x >> 16), (uint16_t)(sv.y & 0xFFFFu),
                                     (uint16_t)(sv.y >> 16)};
-            float xv[16];
+            float xv[MT][16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xv[4 * i] = xr[i].x, xv[4 * i + 1] = xr[i].y, xv[4 * i + 2] = xr[i].z, xv[4 * i + 3] = xr[i].w;
-            }
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xv[t][4 * i] = xr[t][i].x, xv[t][4 * i + 1] = xr[t][i].y;
+                    xv[t][4 * i + 2] = xr[t][i].z, xv[t][4 * i + 3] = xr[t][i].w;
+                }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 h2 p[8];
                 word_m1(cw[r], magic, p);
-                float s = 0.0f;
+                const float d = (float)__builtin_bit_cast(_Float16, db[r]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    s = __builtin_fmaf(xv[2 * i], (float)p[i].x, s);
-                    s = __builtin_fmaf(xv[2 * i + 1], (float)p[i].y, s);
+                for (int t = 0; t < MT; ++t) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        s = __builtin_fmaf(xv[t][2 * i], (float)p[i].x, s);
+                        s = __builtin_fmaf(xv[t][2 * i + 1], (float)p[i].y, s);
+                    }
+                    acc[r][t] = __builtin_fmaf(s, d, acc[r][t]);
                 }
-                acc[r] = __builtin_fmaf(s, (float)__builtin_bit_cast(_Float16, db[r]), acc[r]);
             }
         }
     }
-    // rows r and r+2 pairwise across the lane halves, then across 16-lane rows,
-    // then DPP within each 16-lane row: row k16 + 2*k32's wave sum in lane 16*j
+    // per activation row: rows r and r+2 pairwise across the lane halves, then
+    // across 16-lane rows, then DPP within each 16-lane row: row k16 + 2*k32's
+    // wave sum in lane 16*j
     const int k32 = kept32(), k16 = kept16();
-    float s1[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        float a = acc[r], b = acc[r + 2];
-        swap32(a, b);
-        s1[r] = a + b;
+    for (int t = 0; t < MT; ++t) {
+        float s1[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float a = acc[r][t], b = acc[r + 2][t];
+            swap32(a, b);
+            s1[r] = a + b;
+        }
+        float a = s1[0], b = s1[1];
+        swap16(a, b);
+        const float v = row16_sum(a + b);
+        if ((lane & 15) == 0) red[wave][k16 + 2 * k32][t] = v;
     }
-    float a = s1[0], b = s1[1];
-    swap16(a, b);
-    const float v = row16_sum(a + b);
-    if ((lane & 15) == 0) red[wave][k16 + 2 * k32] = v;
     __syncthreads();
-    if (threadIdx.x < 4 * Q) {
-        const int q = threadIdx.x >> 2, r = threadIdx.x & 3;
-        const float out = (red[4 * q][r] + red[4 * q + 1][r]) + (red[4 * q + 2][r] + red[4 * q + 3][r]);
-        if (row0 + 4 * q + r < N) y[row0 + 4 * q + r] = out;
+    if (threadIdx.x < 4 * Q * MT) {
+        const int q = threadIdx.x / (4 * MT), r = (threadIdx.x / MT) % 4, t = threadIdx.x % MT;
+        const float out = (red[4 * q][r][t] + red[4 * q + 1][r][t]) + (red[4 * q + 2][r][t] + red[4 * q + 3][r][t]);
+        if (row0 + 4 * q + r < N) y[(int64_t)t * N + row0 + 4 * q + r] = out;
     }
 }
 
@@ -264,14 +283,28 @@ static hipError_t gemv_launch(const DevWeight &w, const float *x, float *y, int6
     return hipSuccess;
 }
 
+template <int MT>
+static hipError_t gemv_mt_launch(const DevWeight &w, const float *x, float *y, hipStream_t s) {
+    constexpr int Q = 2;  // Npad is a multiple of 256, so of 4*Q
+    gemv_mt_kernel<Q, MT><<<dim3((unsigned)(w.Npad / (4 * Q))), dim3(256 * Q), 0, s>>>(w.codes, w.scales, x, y,
+                                                                                    (int)w.N, (int)w.K);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s) {
-    if (M == 1) {
-        constexpr int Q = 2;  // Npad is a multiple of 256, so of 4*Q
-        gemv_m1_kernel<Q><<<dim3((unsigned)(w.Npad / (4 * Q))), dim3(256 * Q), 0, s>>>(w.codes, w.scales, x, y,
-                                                                                     (int)w.N, (int)w.K);
-        return hipGetLastError();
+    if (M == 1) return gemv_mt_launch<1>(w, x, y, s);
+    // 2 <= M <= 4: every wave reads all M rows of x for its K range, so with
+    // many weight rows x traffic outweighs the weight's; measured with cold
+    // weights at K = 4096, four rows per lane win up to N = 4096 (M = 2, 3, 4:
+    // 4.96, 6.1, 6.84 us against 5.34, 7.3, 7.4) and eight rows per lane from
+    // N = 8192 (M = 2: 7.40 against 7.59 us; N = 14336: 11.0 against 11.9).
+    if (M <= 4 && w.Npad <= 4096) {
+        if (M == 2) return gemv_mt_launch<2>(w, x, y, s);
+        if (M == 3) return gemv_mt_launch<3>(w, x, y, s);
+        return gemv_mt_launch<4>(w, x, y, s);
     }
     if (M == 2) return gemv_launch<8, 2>(w, x, y, M, s);
+    // more rows (M > 4 when the f32 path is forced): tiles of four activation rows
     return gemv_launch<8, 4>(w, x, y, M, s);
 }
 

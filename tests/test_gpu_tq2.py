@@ -212,6 +212,31 @@ def test_x_beyond_2gb_uses_64bit_addresses(torch):
     check_tq2_sampled(aos, n, k, x, "mfma", "x beyond 2 GB", count=2048)
 
 
+@pytest.mark.parametrize("n,k", [(1000, 4096), (1000, 4608), (5000, 4096)])
+def test_f32_path_up_to_four_rows(torch, n, k):
+    """M = 1..4 on the f32 path: all activation rows in one launch with four weight rows
+    per lane (N = 1000, a ragged last workgroup; K = 4608 takes a second, partial
+    4096-wide pass), or eight weight rows per lane (N = 5000, past 4096 rows, for
+    M = 2..4). Full comparison with the oracle at the f32 bound; with four rows per lane,
+    M = 2..4 give each row's bits of the M = 1 call on that row alone."""
+    aos = wl.sweep_weight(n, k)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        x4 = wl.sweep_x(4, k)
+        singles = [run_tq2(w, x4[i:i + 1].copy(), "f32") for i in range(4)]
+        for m in (1, 2, 3, 4):
+            note(f"[f32 M<=4] M={m} N={n} K={k}")
+            x = x4[:m].copy()
+            y = run_tq2(w, x, "f32")
+            y64, b = oracle.gemm(aos, n, k, x)
+            assert_within(y, y64, b, F32_REL, f"f32 M={m} N={n} K={k}")
+            if n <= 4096:
+                for i in range(m):
+                    assert np.array_equal(y[i].view(np.uint32), singles[i][0].view(np.uint32)), f"row {i} of M={m}"
+    finally:
+        w.close()
+
+
 @pytest.mark.parametrize("path", ["f32", "mfma"])
 def test_many_rows(torch, path):
     """M = 300000 rows: the f32 path's grid runs in slices of 65535 row tiles, and the
