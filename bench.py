@@ -306,17 +306,29 @@ def calib_copy(torch, reps=5):
     torch.cuda.synchronize()
 
 
-def summarize_stats(csv_path, command):
-    """Text summary of a rocprofv3 --stats kernel table (average duration per kernel)."""
+def summarize_stats(csv_path, command, trace_path=None):
+    """Text summary of a rocprofv3 --stats kernel table (average duration per kernel), with
+    each kernel's median duration from the kernel trace when one is given (the median is
+    not moved by the few dispatches the profiler itself delays)."""
     import csv
 
     rows = list(csv.DictReader(open(csv_path)))
+    med = {}
+    if trace_path:
+        durs = {}
+        for r in csv.DictReader(open(trace_path)):
+            durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        med = {k: float(np.median(v)) / 1e3 for k, v in durs.items()}
     print(f"# rocprofv3 kernel statistics")
     print(f"# command: {command}")
-    print(f"# {'kernel':<90s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    print(f"# {'kernel':<90s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"
+          + (f" {'median_us':>9s}" if med else ""))
     for r in rows:
-        print(f"  {r['Name'][:90]:<90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.3f} "
-              f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+        line = (f"  {r['Name'][:90]:<90s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.3f} "
+                f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+        if med:
+            line += f" {med.get(r['Name'], float('nan')):9.3f}"
+        print(line)
 
 
 def summarize_pmc(fetch_csv, write_csv, kernel, command_fetch, command_write):
@@ -420,7 +432,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="decode,prefill,mlp,dit,blr,dense,cpu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
+    ap.add_argument("--summarize-stats", nargs="+", metavar="CSV COMMAND [TRACE_CSV]",
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "CMD_F", "CMD_W"),
                     help="print HBM traffic per launch from two counter runs and exit")
