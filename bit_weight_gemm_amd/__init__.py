@@ -6,9 +6,15 @@ There is no CPU fallback: if the library is missing or fails to load, the calls
 raise.
 
 Names follow the C ABI in include/libtq2.h: tq2_upload, tq2_free, tq2_gemm,
-tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_backward_paths,
-blr_workspace_size, blr_backward_workspace_size, tq2_select_path,
-tq2_set_m_small, tq2_strerror, tq2_version.
+tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_backward_paths
+(library-owned workspace), blr_forward_ws, blr_forward_paths_ws,
+blr_backward_paths_ws (caller-owned workspace), blr_workspace_size,
+blr_backward_workspace_size, tq2_workspace_allocs, tq2_select_path,
+tq2_set_path, tq2_set_m_small, tq2_strerror, tq2_version.
+
+Every tensor's shape is checked here against the sizes the call derives from x,
+h and l before anything reaches the library: the C ABI takes raw device
+pointers and cannot see buffer sizes.
 """
 
 from __future__ import annotations
@@ -66,12 +72,19 @@ def lib():
         "tq2_select_path": ([i64], i32),
         "tq2_set_m_small": ([i64], i64),
         "tq2_dequant": ([p, p, p], i32),
+        "tq2_set_path": ([i32], i32),
+        "tq2_workspace_allocs": ([], ctypes.c_uint64),
         "blr_workspace_size": ([i64, i64, i64, i64], sz),
-        "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
-        "blr_forward_paths": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p], i32),
+        "blr_forward_paths": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p], i32),
+        "blr_forward_ws": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "blr_forward_paths_ws": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
         "blr_backward_workspace_size": ([i64, i64, i64, i64], sz),
-        "blr_backward_paths": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
-        "blr_backward": ([p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
+        "blr_backward_paths": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p], i32),
+        "blr_backward": ([p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p], i32),
+        "blr_backward_paths_ws": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz,
+                                   p], i32),
+        "blr_backward_ws": ([p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
         "tq2_strerror": ([i32], ctypes.c_char_p),
         "tq2_version": ([], ctypes.c_char_p),
     }
@@ -122,6 +135,19 @@ def tq2_select_path(m: int) -> int:
 
 def tq2_set_m_small(v: int) -> int:
     return int(lib().tq2_set_m_small(int(v)))
+
+
+def tq2_set_path(path: int) -> int:
+    """Force the path of every auto call (TQ2_PATH_AUTO restores the choice by M); returns the old setting."""
+    st = int(lib().tq2_set_path(int(path)))
+    if st < 0:
+        raise Tq2Error(st, "tq2_set_path")
+    return st
+
+
+def tq2_workspace_allocs() -> int:
+    """Device allocations the library has made for its own (grow-only) workspaces."""
+    return int(lib().tq2_workspace_allocs())
 
 
 def blr_workspace_size(m: int, d_in: int, d_out: int, r: int) -> int:
@@ -205,79 +231,136 @@ def tq2_dequant(w: Tq2Weight, out=None, stream=None):
     return out
 
 
-def blr_forward(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
-    """Binary low-rank layer forward; bits_* are int32 tensors holding the u32 bitmap words."""
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _blr_sizes(bits_u, bits_v, h, l, g, x, paths: bool):
+    """(P, M, d_in, d_out, r) from x, h and l, with every operand's shape checked
+    against them (bits as int32 words: [P][d_out][r/32] and [P][d_in][r/32])."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, d_in]")
+    m, d_in = x.shape
+    if paths:
+        if h.dim() != 2 or l.dim() != 2:
+            raise ValueError("h and l must be [P, d_out] and [P, r]")
+        npaths, d_out = h.shape
+        r = l.shape[1]
+        lead = (npaths,)
+    else:
+        if h.dim() != 1 or l.dim() != 1:
+            raise ValueError("h and l must be [d_out] and [r]")
+        npaths, d_out, r = 1, h.shape[0], l.shape[0]
+        lead = ()
+    if r % 32:
+        raise ValueError(f"r must be a multiple of 32, got {r}")
+    _shape(l, lead + (r,), "l")
+    _shape(g, lead + (d_in,), "g")
+    _shape(bits_u, lead + (d_out, r // 32), "bits_u")
+    _shape(bits_v, lead + (d_in, r // 32), "bits_v")
+    return npaths, m, d_in, d_out, r
+
+
+def _workspace(workspace, need, like, stream, what):
+    """A caller workspace checked for size, or a temporary one tied to `stream`."""
     import torch
 
-    m, d_in = x.shape
-    d_out, r = h.numel(), l.numel()
+    if need == 0:
+        raise Tq2Error(TQ2_EINVAL, what)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=like.device)
+        if stream is not None and hasattr(stream, "cuda_stream"):
+            workspace.record_stream(stream)  # not reused before the work queued on `stream` is done
+    if workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {workspace.numel()}")
+    return workspace
+
+
+def _blr_forward_call(bits_u, bits_v, h, l, g, x, y, stream, paths: bool, workspace=None, use_ws=False):
+    import torch
+
+    npaths, m, d_in, d_out, r = _blr_sizes(bits_u, bits_v, h, l, g, x, paths)
     if y is None:
         y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
-    need = blr_workspace_size(m, d_in, d_out, r)
-    if need == 0:
-        raise Tq2Error(TQ2_EINVAL, "blr_workspace_size")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(lib().blr_forward(_dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
-                             _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
-                             _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
-                             _dev(y, torch.float32, "y"), m, d_in, d_out, r,
-                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
-           "blr_forward")
+    _shape(y, (m, d_out), "y")
+    args = [_dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"), _dev(h, torch.float32, "h"),
+            _dev(l, torch.float32, "l"), _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
+            _dev(y, torch.float32, "y"), m, d_in, d_out, r]
+    if use_ws:
+        ws = _workspace(workspace, blr_workspace_size(m, d_in, d_out, r), x, stream, "blr_workspace_size")
+        args += [_dev(ws, torch.uint8, "workspace"), ws.numel()]
+    args.append(_stream(stream))
+    L = lib()
+    if paths:
+        fn = L.blr_forward_paths_ws if use_ws else L.blr_forward_paths
+        _check(fn(npaths, *args), fn.__name__)
+    else:
+        fn = L.blr_forward_ws if use_ws else L.blr_forward
+        _check(fn(*args), fn.__name__)
     return y
 
 
-def blr_forward_paths(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
+def blr_forward(bits_u, bits_v, h, l, g, x, y=None, stream=None):
+    """Binary low-rank layer forward (library-owned workspace); bits_* are int32
+    tensors holding the u32 bitmap words [d_out][r/32] and [d_in][r/32]."""
+    return _blr_forward_call(bits_u, bits_v, h, l, g, x, y, stream, paths=False)
+
+
+def blr_forward_ws(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
+    """blr_forward with a caller-owned workspace (uint8, >= blr_workspace_size bytes)."""
+    return _blr_forward_call(bits_u, bits_v, h, l, g, x, y, stream, paths=False, workspace=workspace, use_ws=True)
+
+
+def blr_forward_paths(bits_u, bits_v, h, l, g, x, y=None, stream=None):
     """A layer of P paths, y = sum_p h_p . c_p, rounded path by path; the per-path
     operands are stacked along a leading P axis (bits_u [P][d_out][r/32], bits_v
     [P][d_in][r/32], h [P][d_out], l [P][r], g [P][d_in])."""
-    import torch
+    return _blr_forward_call(bits_u, bits_v, h, l, g, x, y, stream, paths=True)
 
-    m, d_in = x.shape
-    npaths, d_out = h.shape
-    r = l.shape[1]
-    if y is None:
-        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
-    need = blr_workspace_size(m, d_in, d_out, r)
-    if need == 0:
-        raise Tq2Error(TQ2_EINVAL, "blr_workspace_size")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(lib().blr_forward_paths(npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
-                                   _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
-                                   _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
-                                   _dev(y, torch.float32, "y"), m, d_in, d_out, r,
-                                   _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
-           "blr_forward_paths")
-    return y
+
+def blr_forward_paths_ws(bits_u, bits_v, h, l, g, x, y=None, workspace=None, stream=None):
+    return _blr_forward_call(bits_u, bits_v, h, l, g, x, y, stream, paths=True, workspace=workspace, use_ws=True)
 
 
 def blr_backward_workspace_size(m: int, d_in: int, d_out: int, r: int) -> int:
     return int(lib().blr_backward_workspace_size(m, d_in, d_out, r))
 
 
-def blr_backward_paths(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx=None, gscale=1024.0, workspace=None,
-                       stream=None):
-    """Backward of blr_forward_paths on the same x: dh [P][d_out], dl [P][r] and dg [P][d_in]
-    are accumulated in place; dx [M][d_in] is overwritten (returned)."""
+def _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, workspace, use_ws):
     import torch
 
-    m, d_in = x.shape
-    npaths, d_out = h.shape
-    r = l.shape[1]
+    npaths, m, d_in, d_out, r = _blr_sizes(bits_u, bits_v, h, l, g, x, paths=True)
+    _shape(dy, (m, d_out), "dy")
+    _shape(dh, (npaths, d_out), "dh")
+    _shape(dl, (npaths, r), "dl")
+    _shape(dg, (npaths, d_in), "dg")
     if dx is None:
         dx = torch.empty((m, d_in), dtype=torch.float32, device=x.device)
-    need = blr_backward_workspace_size(m, d_in, d_out, r)
-    if need == 0:
-        raise Tq2Error(TQ2_EINVAL, "blr_backward_workspace_size")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(lib().blr_backward_paths(npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
-                                    _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"),
-                                    _dev(g, torch.float32, "g"), _dev(x, torch.float32, "x"),
-                                    _dev(dy, torch.float32, "dy"), _dev(dx, torch.float32, "dx"),
-                                    _dev(dh, torch.float32, "dh"), _dev(dl, torch.float32, "dl"),
-                                    _dev(dg, torch.float32, "dg"), m, d_in, d_out, r, float(gscale),
-                                    _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
-           "blr_backward_paths")
+    _shape(dx, (m, d_in), "dx")
+    args = [npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
+            _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"), _dev(g, torch.float32, "g"),
+            _dev(x, torch.float32, "x"), _dev(dy, torch.float32, "dy"), _dev(dx, torch.float32, "dx"),
+            _dev(dh, torch.float32, "dh"), _dev(dl, torch.float32, "dl"), _dev(dg, torch.float32, "dg"),
+            m, d_in, d_out, r, float(gscale)]
+    L = lib()
+    if use_ws:
+        ws = _workspace(workspace, blr_backward_workspace_size(m, d_in, d_out, r), x, stream,
+                        "blr_backward_workspace_size")
+        _check(L.blr_backward_paths_ws(*args, _dev(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)),
+               "blr_backward_paths_ws")
+    else:
+        _check(L.blr_backward_paths(*args, _stream(stream)), "blr_backward_paths")
     return dx
+
+
+def blr_backward_paths(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx=None, gscale=1024.0, stream=None):
+    """Backward of blr_forward_paths on the same x (library-owned workspace): dh [P][d_out],
+    dl [P][r] and dg [P][d_in] are accumulated in place; dx [M][d_in] is overwritten (returned)."""
+    return _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, None, False)
+
+
+def blr_backward_paths_ws(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx=None, gscale=1024.0, workspace=None,
+                          stream=None):
+    """blr_backward_paths with a caller-owned workspace (uint8, >= blr_backward_workspace_size bytes)."""
+    return _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, workspace, True)

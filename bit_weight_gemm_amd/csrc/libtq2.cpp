@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -90,6 +91,53 @@ inline uint32_t group_word(const uint8_t *qs4) {
     return out;
 }
 
+
+// Library-owned workspaces: one grow-only device buffer per (device, stream),
+// kept until the process ends.  Calls on one stream are ordered by the stream,
+// so they can share its buffer; a host-side lock is held from the size check
+// until the launches are queued, so two host threads on one stream cannot free
+// a buffer the other is about to use.
+struct Pool {
+    int dev = -1;
+    hipStream_t stream = nullptr;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    std::mutex mu;
+};
+std::mutex g_pools_mu;
+std::vector<std::unique_ptr<Pool>> g_pools;
+std::atomic<uint64_t> g_ws_allocs{0};  // device allocations made for workspaces
+
+Pool &pool_for(int dev, hipStream_t s) {
+    std::lock_guard<std::mutex> lock(g_pools_mu);
+    for (auto &p : g_pools)
+        if (p->dev == dev && p->stream == s) return *p;
+    g_pools.emplace_back(new Pool);
+    g_pools.back()->dev = dev;
+    g_pools.back()->stream = s;
+    return *g_pools.back();
+}
+
+// At least `need` bytes in the pool (call with pool.mu held).  Growing frees the
+// old buffer first; hipFree waits for the device, so the work queued earlier on
+// the stream has finished with it.
+int pool_reserve(Pool &p, size_t need) {
+    if (p.bytes >= need) return TQ2_OK;
+    if (p.ptr) {
+        const hipError_t e = hipFree(p.ptr);
+        p.ptr = nullptr;
+        p.bytes = 0;
+        if (e != hipSuccess) return from_hip(e);
+    }
+    void *m = nullptr;
+    const hipError_t e = hipMalloc(&m, need);
+    if (e != hipSuccess) return from_hip(e);
+    p.ptr = m;
+    p.bytes = need;
+    g_ws_allocs.fetch_add(1);
+    return TQ2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,6 +161,13 @@ int64_t tq2_set_m_small(int64_t v) {
     return old;
 }
 
+int tq2_set_path(int path) {
+    if (path < TQ2_PATH_AUTO || path > TQ2_PATH_MFMA) return TQ2_EINVAL;
+    const int old = forced_path();
+    g_forced.store(path);
+    return old;
+}
+
 int tq2_select_path(int64_t M) {
     const int f = forced_path();
     if (f) return f;
@@ -123,7 +178,8 @@ int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *strea
     if (!aos || !out) return TQ2_EINVAL;
     if (N < 1 || K < tq2::kBlock || K % tq2::kBlock) return TQ2_EINVAL;
     const int64_t kb = K / tq2::kBlock;
-    if (N > (int64_t)1 << 31 || K > (int64_t)1 << 30) return TQ2_EINVAL;
+    // kernels index rows with 32-bit integers: the padded row count must fit
+    if (N > ((int64_t)1 << 31) - tq2::kRowPad || K > (int64_t)1 << 30) return TQ2_EINVAL;
     if (nbytes != (size_t)N * (size_t)kb * kBlockBytes) return TQ2_EINVAL;
     *out = nullptr;
     int dev = -1;
@@ -262,72 +318,70 @@ size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     return tq2::blr_plan(M, d_in, d_out, r).total;
 }
 
-// Host-side checks shared by the BLR entry points: P stacked paths of the given
-// sizes (P = 1 for blr_forward).  Returns TQ2_OK or the status to report.
-static int blr_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
-                     const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
-                     void *workspace, size_t workspace_bytes) {
-    const size_t need = blr_workspace_size(M, d_in, d_out, r);
-    if (need == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
-    if (!bits_u || !bits_v || !h || !l || !g || !x || !y || !workspace) return TQ2_EINVAL;
-    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TQ2_EINVAL;
-    if (!aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(bits_u) & 3u) ||
-        (reinterpret_cast<uintptr_t>(bits_v) & 3u) || (reinterpret_cast<uintptr_t>(h) & 3u) ||
-        (reinterpret_cast<uintptr_t>(l) & 3u) || (reinterpret_cast<uintptr_t>(g) & 3u))
-        return TQ2_EINVAL;
-    const size_t ybytes = (size_t)M * d_out * 4, p = (size_t)P;
-    if (overlap(y, ybytes, x, (size_t)M * d_in * 4) || overlap(y, ybytes, workspace, need) ||
-        overlap(y, ybytes, bits_u, p * d_out * (r / 32) * 4) || overlap(y, ybytes, bits_v, p * d_in * (r / 32) * 4) ||
-        overlap(y, ybytes, h, p * d_out * 4) || overlap(y, ybytes, l, p * r * 4) || overlap(y, ybytes, g, p * d_in * 4))
-        return TQ2_EINVAL;
-    return TQ2_OK;
-}
-
-int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
-                const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *workspace,
-                size_t workspace_bytes, void *stream) {
-    return blr_forward_paths(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace, workspace_bytes, stream);
-}
-
-int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
-                      const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
-                      void *workspace, size_t workspace_bytes, void *stream) {
-    if (blr_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
-    int dev = -1;
-    int st = check_device(&dev);
-    if (st) return st;
-    if (M == 0) return TQ2_OK;
-    st = blr_check(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace, workspace_bytes);
-    if (st) return st;
-    const tq2::BlrPlan plan = tq2::blr_plan(M, d_in, d_out, r);
-    const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
-    for (int64_t p = 0; p < P; ++p) {
-        st = from_hip(tq2::launch_blr_forward(plan, bits_u + p * wu, bits_v + p * wv, h + p * d_out, l + p * r,
-                                              g + p * d_in, x, y, workspace, p > 0, static_cast<hipStream_t>(stream)));
-        if (st) return st;
-    }
-    return TQ2_OK;
-}
-
 size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     if (blr_workspace_size(M, d_in, d_out, r) == 0) return 0;
     return tq2::blr_bwd_plan(M, d_in, d_out, r).total;
 }
 
-int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
-                       const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
-                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
-                       size_t workspace_bytes, void *stream) {
-    const size_t need = blr_backward_workspace_size(M, d_in, d_out, r);
-    if (need == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16) return TQ2_EINVAL;  // token chunks fit grid.y
+uint64_t tq2_workspace_allocs(void) { return g_ws_allocs.load(); }
+
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a BLR forward: P stacked paths of the given sizes, every
+// pointer and alignment, and y overlapping none of the inputs.  The workspace is
+// checked by the caller (it may be the library's own).
+int blr_forward_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                      const float *g, const float *x, const float *y, int64_t M, int64_t d_in, int64_t d_out,
+                      int64_t r) {
+    if (blr_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
+    if (M == 0) return TQ2_OK;
+    if (!bits_u || !bits_v || !h || !l || !g || !x || !y) return TQ2_EINVAL;
+    if (!aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(bits_u) & 3u) ||
+        (reinterpret_cast<uintptr_t>(bits_v) & 3u) || (reinterpret_cast<uintptr_t>(h) & 3u) ||
+        (reinterpret_cast<uintptr_t>(l) & 3u) || (reinterpret_cast<uintptr_t>(g) & 3u))
+        return TQ2_EINVAL;
+    const size_t ybytes = (size_t)M * d_out * 4, p = (size_t)P;
+    if (overlap(y, ybytes, x, (size_t)M * d_in * 4) || overlap(y, ybytes, bits_u, p * d_out * (r / 32) * 4) ||
+        overlap(y, ybytes, bits_v, p * d_in * (r / 32) * 4) || overlap(y, ybytes, h, p * d_out * 4) ||
+        overlap(y, ybytes, l, p * r * 4) || overlap(y, ybytes, g, p * d_in * 4))
+        return TQ2_EINVAL;
+    return TQ2_OK;
+}
+
+// The caller's workspace: large enough, 256-byte aligned, not overlapping the output.
+int workspace_check(const void *ws, size_t ws_bytes, size_t need, const void *out, size_t out_bytes) {
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return TQ2_EINVAL;
+    if (overlap(out, out_bytes, ws, need)) return TQ2_EINVAL;
+    return TQ2_OK;
+}
+
+// The paths one after another, sharing one path's workspace (checked arguments).
+int blr_forward_launch(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                       const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                       void *workspace, hipStream_t s) {
+    const tq2::BlrPlan plan = tq2::blr_plan(M, d_in, d_out, r);
+    const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
+    for (int64_t p = 0; p < P; ++p) {
+        const int st = from_hip(tq2::launch_blr_forward(plan, bits_u + p * wu, bits_v + p * wv, h + p * d_out,
+                                                        l + p * r, g + p * d_in, x, y, workspace, p > 0, s));
+        if (st) return st;
+    }
+    return TQ2_OK;
+}
+
+// Host-side checks of a BLR backward (everything but the workspace).
+int blr_backward_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                       const float *g, const float *x, const float *dy, const float *dx, const float *dh,
+                       const float *dl, const float *dg, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                       float gscale) {
+    if (blr_backward_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16)
+        return TQ2_EINVAL;  // token chunks fit grid.y
     int e2 = 0;
     if (!std::isfinite(gscale) || gscale <= 0.0f || std::frexp(gscale, &e2) != 0.5f || gscale > 65536.0f)
         return TQ2_EINVAL;  // a power of two, at most 2^16
-    int dev = -1;
-    int st = check_device(&dev);
-    if (st) return st;
-    if (!bits_u || !bits_v || !h || !l || !g || !x || !dy || !dx || !dh || !dl || !dg || !workspace) return TQ2_EINVAL;
-    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TQ2_EINVAL;
+    if (!bits_u || !bits_v || !h || !l || !g || !x || !dy || !dx || !dh || !dl || !dg) return TQ2_EINVAL;
     const uintptr_t mis = reinterpret_cast<uintptr_t>(bits_u) | reinterpret_cast<uintptr_t>(bits_v) |
                           reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(g) |
                           reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
@@ -338,8 +392,7 @@ int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v
     struct Span { const void *ptr; size_t bytes; };
     const Span outs[] = {{dx, (size_t)M * d_in * 4}, {dh, p * d_out * 4}, {dl, p * r * 4}, {dg, p * d_in * 4}};
     const Span ins[] = {{bits_u, p * d_out * (r / 32) * 4}, {bits_v, p * d_in * (r / 32) * 4}, {h, p * d_out * 4},
-                        {l, p * r * 4}, {g, p * d_in * 4}, {x, (size_t)M * d_in * 4}, {dy, (size_t)M * d_out * 4},
-                        {workspace, need}};
+                        {l, p * r * 4}, {g, p * d_in * 4}, {x, (size_t)M * d_in * 4}, {dy, (size_t)M * d_out * 4}};
     for (size_t i = 0; i < 4; ++i) {
         for (const Span &in : ins)
             if (outs[i].bytes && in.bytes && overlap(outs[i].ptr, outs[i].bytes, in.ptr, in.bytes)) return TQ2_EINVAL;
@@ -347,23 +400,127 @@ int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v
             if (outs[i].bytes && outs[j].bytes && overlap(outs[i].ptr, outs[i].bytes, outs[j].ptr, outs[j].bytes))
                 return TQ2_EINVAL;
     }
-    if (M == 0) return TQ2_OK;  // no tokens: no gradient to add, dx is empty
+    return TQ2_OK;
+}
+
+// The caller's backward workspace must also stay clear of all four outputs.
+int backward_workspace_check(const void *ws, size_t ws_bytes, size_t need, int64_t P, const float *dx,
+                             const float *dh, const float *dl, const float *dg, int64_t M, int64_t d_in,
+                             int64_t d_out, int64_t r) {
+    const size_t p = (size_t)P;
+    int st = workspace_check(ws, ws_bytes, need, dx, (size_t)M * d_in * 4);
+    if (!st) st = workspace_check(ws, ws_bytes, need, dh, p * d_out * 4);
+    if (!st) st = workspace_check(ws, ws_bytes, need, dl, p * r * 4);
+    if (!st) st = workspace_check(ws, ws_bytes, need, dg, p * d_in * 4);
+    return st;
+}
+
+int blr_backward_launch(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                        const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                        int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
+                        hipStream_t s) {
     const tq2::BlrBwdPlan plan = tq2::blr_bwd_plan(M, d_in, d_out, r);
     const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
     for (int64_t q = 0; q < P; ++q) {
-        st = from_hip(tq2::launch_blr_backward(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out, l + q * r,
-                                               g + q * d_in, x, dy, dx, dh + q * d_out, dl + q * r, dg + q * d_in,
-                                               gscale, workspace, q > 0, static_cast<hipStream_t>(stream)));
+        const int st = from_hip(tq2::launch_blr_backward(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out,
+                                                         l + q * r, g + q * d_in, x, dy, dx, dh + q * d_out,
+                                                         dl + q * r, dg + q * d_in, gscale, workspace, q > 0, s));
         if (st) return st;
     }
     return TQ2_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int blr_forward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                         const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    int st = blr_forward_check(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    st = workspace_check(workspace, workspace_bytes, blr_workspace_size(M, d_in, d_out, r), y, (size_t)M * d_out * 4);
+    if (st) return st;
+    return blr_forward_launch(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace,
+                              static_cast<hipStream_t>(stream));
+}
+
+int blr_forward_ws(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                   const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return blr_forward_paths_ws(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, workspace, workspace_bytes,
+                                stream);
+}
+
+int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                      const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                      void *stream) {
+    int st = blr_forward_check(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Pool &pool = pool_for(dev, s);
+    std::lock_guard<std::mutex> lock(pool.mu);  // held until the launches are queued
+    st = pool_reserve(pool, blr_workspace_size(M, d_in, d_out, r));
+    if (st) return st;
+    return blr_forward_launch(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, pool.ptr, s);
+}
+
+int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *stream) {
+    return blr_forward_paths(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, stream);
+}
+
+int blr_backward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                          const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                          int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    int st = blr_backward_check(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st) return st;
+    const size_t need = blr_backward_workspace_size(M, d_in, d_out, r);
+    st = backward_workspace_check(workspace, workspace_bytes, need, P, dx, dh, dl, dg, M, d_in, d_out, r);
+    if (st || M == 0) return st;  // no tokens: no gradient to add, dx is empty
+    return blr_backward_launch(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale,
+                               workspace, static_cast<hipStream_t>(stream));
+}
+
+int blr_backward_ws(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                    const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M,
+                    int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return blr_backward_paths_ws(1, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale,
+                                 workspace, workspace_bytes, stream);
+}
+
+int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                       const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *stream) {
+    int st = blr_backward_check(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Pool &pool = pool_for(dev, s);
+    std::lock_guard<std::mutex> lock(pool.mu);
+    st = pool_reserve(pool, blr_backward_workspace_size(M, d_in, d_out, r));
+    if (st) return st;
+    return blr_backward_launch(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale, pool.ptr,
+                               s);
+}
+
 int blr_backward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
                  const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M, int64_t d_in,
-                 int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes, void *stream) {
-    return blr_backward_paths(1, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale,
-                              workspace, workspace_bytes, stream);
+                 int64_t d_out, int64_t r, float gscale, void *stream) {
+    return blr_backward_paths(1, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale, stream);
 }
 
 }  // extern "C"

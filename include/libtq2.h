@@ -61,7 +61,7 @@ typedef struct tq2_weight tq2_weight;
 
 /* [TQ2] weight upload.  `aos` is host memory holding N*(K/128) blocks of 34 bytes,
  * row-major over (row, block): 32 code bytes then the f16 scale, little-endian.
- * Requires N >= 1, K >= 128, K % 128 == 0, nbytes == N*(K/128)*34 and every scale
+ * Requires 1 <= N <= 2^31 - 256, 128 <= K <= 2^30, K % 128 == 0, nbytes == N*(K/128)*34 and every scale
  * finite (a NaN or infinite scale is TQ2_EINVAL).  The bytes are repacked on the
  * host into the device layout and copied on `stream`; the call returns after the
  * copy has completed, so `aos` may be freed at once.  *out receives the handle. */
@@ -83,8 +83,14 @@ int tq2_weight_info(const tq2_weight *w, int64_t *N, int64_t *K, size_t *device_
 int tq2_gemm(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* tq2_gemm on an explicitly chosen path (TQ2_PATH_AUTO, _F32 or _MFMA).
- * The MFMA path needs |x| <= 65504 (f16 range; not checked).  A weight holding a
- * code-3 weight whose scale has |d| > 32752 (2d beyond f16) runs on the f32 path. */
+ * The MFMA path rounds x to f16 (nearest even) and needs |x| <= 65504 (not
+ * checked).  Its per-output bound 4e-3 * sum_k |x*w| holds when that rounding is
+ * relative, i.e. every nonzero |x| >= 2^-14 (f16 normal range); smaller values
+ * become f16 subnormals whose rounding error is up to 2^-25 absolute, so a row
+ * of x made only of such values (|x| below ~1e-5) can miss the relative bound:
+ * run those on the f32 path (or scale x by a power of two first).  A weight
+ * holding a code-3 weight whose scale has |d| > 32752 (2d beyond f16) runs on
+ * the f32 path. */
 int tq2_gemm_path(const tq2_weight *w, const float *x, float *y, int64_t M, int64_t N, int64_t K,
                   int path, void *stream);
 
@@ -96,13 +102,18 @@ int tq2_select_path(int64_t M);
 /* Sets the auto-path threshold (M <= m_small runs on the f32 path); returns the old one. */
 int64_t tq2_set_m_small(int64_t m_small);
 
+/* Forces the path of every TQ2_PATH_AUTO call in the process (tq2_gemm):
+ * TQ2_PATH_AUTO (0) restores the choice by M, TQ2_PATH_F32 (1) or TQ2_PATH_MFMA
+ * (2) forces that path (the env variable TQ2_PATH=f32|mfma sets the initial
+ * value).  Returns the previous setting, or TQ2_EINVAL for another value.  The
+ * page validates each kernel variant through helpers that bypass the public
+ * dispatch; this is the same switch for a whole process. */
+int tq2_set_path(int path);
+
 /* [TQ2] decode on the GPU: w_out[n][k] = (code-1)*d as f32, device [N][K] row-major,
  * 16-byte aligned.  Bit-exact with the format's definition (including -0.0 for a
  * zero code under a negative scale).  Asynchronous on `stream`. */
 int tq2_dequant(const tq2_weight *w, float *w_out, void *stream);
-
-/* Bytes of device workspace blr_forward needs for these sizes (0 on bad sizes). */
-size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 
 /* [BLR] y[t][i] = h[i] * sum_k f16(a[t][k]*l[k]) * S_U[i][k],
  *        a[t][k] = sum_j f16(x[t][j]*g[j]) * S_V[j][k]          (f32 accumulation).
@@ -110,13 +121,16 @@ size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
  * bitmaps, 4-byte aligned); h [d_out], l [r], g [d_in]: device f32; x: device f32
  * [M][d_in]; y: device f32 [M][d_out], overwritten, 16-byte aligned, must not
  * overlap the inputs.  Requires d_in >= 1, d_out >= 1, r >= 32, r % 32 == 0, M >= 0
- * (M == 0 is a no-op).  `workspace` is caller-owned device memory of at least
- * blr_workspace_size(...) bytes, 256-byte aligned; its contents are scratch.
+ * (M == 0 is a no-op).  The f16(a*l) intermediate lives in a workspace that the
+ * library owns: one grow-only device buffer per (device, stream), allocated on
+ * first use and enlarged (never shrunk) when a call needs more, kept until the
+ * process ends (tq2_workspace_allocs counts these allocations).  The page's
+ * layer likewise keeps its staging buffers in a scratch object it reuses.
  * Preconditions (not checked): |x*g| and |a*l| within f16 range.
- * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
+ * Asynchronous on `stream`. */
 int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                 const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
-                int64_t r, void *workspace, size_t workspace_bytes, void *stream);
+                int64_t r, void *stream);
 
 /* [BLR] A layer of P paths, y = sum_p h_p . c_p, each path the product of
  * blr_forward with its own bitmaps and vectors (all paths share M, d_in, d_out
@@ -124,16 +138,27 @@ int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, 
  * scale_acc2 kernels round it: y = f32(h_0*c_0), then y = f32(y + f32(h_p*c_p))
  * for p = 1 .. P-1, each product rounded before the addition.  Per-path operands
  * are stacked in device memory: bits_u [P][d_out][r/32], bits_v [P][d_in][r/32],
- * h [P][d_out], l [P][r], g [P][d_in].  Requires P >= 1 and everything
- * blr_forward requires; the workspace is one path's (blr_workspace_size),
- * reused by the paths in turn, so the paths run one after another on `stream`.
- * P == 1 gives blr_forward's result. */
+ * h [P][d_out], l [P][r], g [P][d_in].  Requires 1 <= P <= 4096 and everything
+ * blr_forward requires; the paths run one after another on `stream`, sharing
+ * one path's workspace (the library's, as for blr_forward).  P == 1 gives
+ * blr_forward's result. */
 int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                       const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
-                      void *workspace, size_t workspace_bytes, void *stream);
+                      void *stream);
 
-/* Bytes of device workspace blr_backward / blr_backward_paths need (0 on bad sizes). */
-size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+/* Bytes of device workspace blr_forward_ws / blr_forward_paths_ws need (0 on bad sizes). */
+size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/* blr_forward / blr_forward_paths with a caller-owned workspace instead of the
+ * library's: `workspace` is device memory of at least blr_workspace_size(...)
+ * bytes, 256-byte aligned, not overlapping y; its contents are scratch.  Calls
+ * sharing a workspace must not overlap in time. */
+int blr_forward_ws(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                   const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
+                   int64_t r, void *workspace, size_t workspace_bytes, void *stream);
+int blr_forward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                         const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* [BLR] Backward of blr_forward_paths on the same x, path by path (the page's
  * blr_backward; per path a = (x.g) S_V and c = (a.l) S_U^T as in the forward):
@@ -147,20 +172,43 @@ size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64
  * are accumulated (y = f32(y + s)); dx [M][d_in] is overwritten by path 0 and the
  * later paths add f32(g.dx') to it.  Operands as for blr_forward_paths, plus dy:
  * device f32 [M][d_out]; all device pointers 4-byte aligned and l 16-byte
- * aligned; outputs must not overlap each other, the inputs or the workspace.
- * M <= 1048560 (65535 chunks of 16 tokens); M == 0 is a no-op.
+ * aligned; outputs must not overlap each other or the inputs.
+ * 1 <= P <= 4096; M <= 1048560 (65535 chunks of 16 tokens); M == 0 is a no-op.
+ * The workspace is the library's (as for blr_forward).
  * Preconditions (not checked): the forward's, and |dy.h.gscale| and |db.l.gscale|
  * within f16 range (choose gscale so that they are neither huge nor subnormal).
- * Asynchronous on `stream`; calls sharing a workspace must not overlap. */
+ * Asynchronous on `stream`. */
 int blr_backward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                        const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
-                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
-                       size_t workspace_bytes, void *stream);
+                       int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *stream);
 
 /* [BLR] blr_backward_paths with one path. */
 int blr_backward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
                  const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M, int64_t d_in,
-                 int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes, void *stream);
+                 int64_t d_out, int64_t r, float gscale, void *stream);
+
+/* Bytes of device workspace blr_backward_ws / blr_backward_paths_ws need (0 on bad sizes). */
+size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/* The backward with a caller-owned workspace of at least
+ * blr_backward_workspace_size(...) bytes, 256-byte aligned, not overlapping the
+ * outputs; calls sharing a workspace must not overlap in time. */
+int blr_backward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                          const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
+                          int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
+                          size_t workspace_bytes, void *stream);
+int blr_backward_ws(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                    const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg, int64_t M,
+                    int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Number of device allocations the library has made for its own workspaces
+ * since the process started (grow-only: a call that fits the buffer its
+ * (device, stream) already holds allocates nothing).  The page's GEMM keeps a
+ * pooled buffer set whose allocation count stays constant once warmed up; this
+ * counter lets a caller check the same.  tq2_gemm and tq2_dequant never
+ * allocate. */
+uint64_t tq2_workspace_allocs(void);
 
 /* Static text for a status code. */
 const char *tq2_strerror(int status);

@@ -40,6 +40,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         i64, sz, p = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = ctypes.c_int
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         L.tq2_oracle_dequant.argtypes = [p, sz, i64, i64, p]
@@ -74,6 +76,11 @@ def _check(rc):
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Thread count of later oracle calls (OpenMP); returns the count in force."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 def half_to_double(bits: int) -> float:

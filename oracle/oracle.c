@@ -48,6 +48,18 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Threads of the later parallel regions (the CPU-baseline timing runs the oracle on
+ * one thread and on all of them); returns the count now in force. */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* IEEE 754 binary16 -> double, from the format's definition:
  * sign bit 15, exponent bits 14..10 (bias 15), fraction bits 9..0;
  * exponent 0 encodes subnormals frac * 2^-24, exponent 31 infinities and NaNs. */

@@ -38,8 +38,10 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for must in ("tq2_upload", "tq2_free", "tq2_gemm", "tq2_gemm_path", "tq2_dequant", "blr_forward",
-                 "blr_forward_paths", "blr_workspace_size", "tq2_select_path", "tq2_set_m_small", "tq2_strerror", "tq2_version",
-                 "tq2_weight_info"):
+                 "blr_forward_paths", "blr_backward", "blr_backward_paths", "blr_forward_ws", "blr_forward_paths_ws",
+                 "blr_backward_ws", "blr_backward_paths_ws", "blr_workspace_size", "blr_backward_workspace_size",
+                 "tq2_select_path", "tq2_set_path", "tq2_set_m_small", "tq2_workspace_allocs", "tq2_strerror",
+                 "tq2_version", "tq2_weight_info"):
         assert must in names, must
 
 
@@ -72,6 +74,36 @@ def test_upload_rejects_bad_arguments_on_the_host(L):
     assert L.tq2_upload(aos.ctypes.data_as(ctypes.c_void_p), aos.size, n, k, None, None) == bw.TQ2_EINVAL
 
 
+def test_upload_row_count_limit(L):
+    """Kernels index rows with 32-bit integers: N above 2^31 - 256 (whose padded count
+    would not fit) is refused on the host, before the byte count or any device is
+    looked at (without the check these calls would reach the device check)."""
+    buf = np.zeros(64, np.uint8)
+    out = ctypes.c_void_p()
+    ptr = buf.ctypes.data_as(ctypes.c_void_p)
+    n_max = (1 << 31) - 256
+    assert L.tq2_upload(ptr, (n_max + 1) * 34, n_max + 1, 128, None, ctypes.byref(out)) == bw.TQ2_EINVAL
+    assert L.tq2_upload(ptr, (1 << 31) * 34, 1 << 31, 128, None, ctypes.byref(out)) == bw.TQ2_EINVAL
+
+
+def test_set_path_rejects_unknown_paths(L):
+    assert L.tq2_set_path(3) == bw.TQ2_EINVAL
+    assert L.tq2_set_path(-1) == bw.TQ2_EINVAL
+    old = bw.tq2_set_path(bw.TQ2_PATH_MFMA)
+    try:
+        assert bw.tq2_select_path(1) == bw.TQ2_PATH_MFMA
+        assert bw.tq2_set_path(bw.TQ2_PATH_F32) == bw.TQ2_PATH_MFMA
+        assert bw.tq2_select_path(4096) == bw.TQ2_PATH_F32
+        bw.tq2_set_path(bw.TQ2_PATH_AUTO)
+        assert bw.tq2_select_path(1) == bw.TQ2_PATH_F32 and bw.tq2_select_path(4096) == bw.TQ2_PATH_MFMA
+    finally:
+        bw.tq2_set_path(old)
+
+
+def test_workspace_counter_starts_at_zero_without_a_device(L):
+    assert bw.tq2_workspace_allocs() == 0
+
+
 def test_workspace_size_rules(L):
     assert bw.blr_workspace_size(512, 4096, 4096, 1024) > 512 * 1024 * 4
     assert bw.blr_workspace_size(1, 4096, 4096, 1000) == 0     # r % 32 != 0
@@ -94,10 +126,27 @@ def test_auto_path_threshold(L):
 
 def test_blr_forward_rejects_bad_sizes_on_the_host(L):
     # r % 32 != 0 is refused before any pointer or device is looked at
-    assert L.blr_forward(None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
+    assert L.blr_forward(None, None, None, None, None, None, None, 4, 8, 8, 33, None) == bw.TQ2_EINVAL
+    assert L.blr_forward_ws(None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
     # a layer needs at least one path; bad sizes are refused as for one path
-    assert L.blr_forward_paths(0, None, None, None, None, None, None, None, 4, 8, 8, 32, None, 0, None) == bw.TQ2_EINVAL
-    assert L.blr_forward_paths(2, None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0, None) == bw.TQ2_EINVAL
+    assert L.blr_forward_paths(0, None, None, None, None, None, None, None, 4, 8, 8, 32, None) == bw.TQ2_EINVAL
+    assert L.blr_forward_paths(2, None, None, None, None, None, None, None, 4, 8, 8, 33, None) == bw.TQ2_EINVAL
+    # null operands with tokens present are refused on the host, before any allocation
+    assert L.blr_forward(None, None, None, None, None, None, None, 4, 8, 8, 32, None) == bw.TQ2_EINVAL
+    assert bw.tq2_workspace_allocs() == 0
+
+
+def test_blr_backward_rejects_bad_arguments_on_the_host(L):
+    f = ctypes.c_float
+    # gradient scale not a power of two, r % 32 != 0, no paths
+    assert L.blr_backward(None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8, 32, f(3.0),
+                          None) == bw.TQ2_EINVAL
+    assert L.blr_backward(None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8, 33, f(1.0),
+                          None) == bw.TQ2_EINVAL
+    assert L.blr_backward_paths(0, None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8, 32,
+                                f(1.0), None) == bw.TQ2_EINVAL
+    assert L.blr_backward_paths_ws(1, None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8, 32,
+                                   f(1.0), None, 0, None) == bw.TQ2_EINVAL
 
 
 def test_bench_refuses_more_than_one_gpu():

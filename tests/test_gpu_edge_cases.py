@@ -1,0 +1,158 @@
+"""GPU parity of every kernel template on the block format's edge cases.
+
+The format ("oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs", correctness test):
+each 128-weight block is 32 bytes of 2-bit codes plus an f16 scale d, and
+w = (code - 1) * d.  The weights here (`workloads.edge_weight`) hold, row class
+by row class: all-0x55 blocks (every code 1: the weight is zero, so y must be
+exactly 0), a single nonzero code in a row (y must be exactly +-d*x, rounded
+once on the f32 path; on the MFMA path exactly f16(x)*d, which f32 holds
+exactly), all-0x00 blocks (every weight -d), subnormal, large (up to 32752,
+where 2d is still a finite f16), negative and zero scales, and code 3 (+2d),
+which the page's generator never draws.
+
+Each case lands on one kernel template of the f32 or the MFMA path (the label
+names it) and is compared with the oracle over every output at the path's bound:
+1e-5 * sum_k |x*w| (f32 path), 4e-3 * sum_k |x*w| (MFMA path).  The prefill and
+the smaller DiT shape are also compared in full, not sampled.
+"""
+
+import numpy as np
+import pytest
+
+import bit_weight_gemm_amd as bw
+import oracle
+import workloads as wl
+from gpu_util import F32_REL, MFMA_REL, assert_within, note, run_tq2, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+# (label: the kernel template the case lands on, path, Ms, N, K)
+CASES = [
+    ("gemv_mt M=1, a second partial 4096-wide pass", "f32", (1,), 1000, 4608),
+    ("gemv_mt M=2..4", "f32", (2, 3, 4), 1000, 1024),
+    ("gemv_f32 eight rows per lane, M=2", "f32", (2,), 5000, 1024),
+    ("gemv_f32 eight rows per lane, M=3 and forced M=7", "f32", (3, 7), 5000, 1024),
+    ("skinny, 32-column workgroups (M=16: 32 pieces of x per thread)", "mfma", (1, 8, 16), 1000, 4096),
+    ("skinny, 64-column workgroups", "mfma", (4,), 9000, 2048),
+    ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
+    ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
+    ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
+    ("64x64 tiles, 512-wide steps", "mfma", (40,), 1000, 4096),
+    ("64x64 tiles, four stages", "mfma", (40,), 1000, 1536),
+    ("64x64 tiles, two k groups", "mfma", (40,), 1000, 768),
+    ("32x256 tiles, odd block count", "mfma", (40,), 1000, 384),
+    ("96x256 tiles", "mfma", (200,), 1000, 768),
+    ("128x256 tiles, one k group, odd block count", "mfma", (200,), 1000, 384),
+    ("128x256 tiles, two k groups", "mfma", (1600,), 4096, 768),
+]
+
+
+def _x(m, k, seed):
+    x = np.random.default_rng(seed).standard_normal((m, k)).astype(np.float32)
+    x[:, ::97] = 0.0  # some exact zeros
+    return x
+
+
+def _scale(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _exact_rows(y, x, codes, bits, path):
+    """Rows of class 0 give exactly 0; rows of class 1 exactly the one product."""
+    n, k = codes.shape
+    cls = np.arange(n) % wl.EDGE_CLASSES
+    zero_rows = np.flatnonzero(cls == 0)
+    assert np.all(y[:, zero_rows] == 0.0), "all-0x55 rows must give exactly 0"
+    xs = x.astype(np.float64) if path == "f32" else x.astype(np.float16).astype(np.float64)
+    for row in np.flatnonzero(cls == 1):
+        pos = int(np.flatnonzero(codes[row] != 1)[0])
+        d = _scale(bits[row, pos // wl.BLOCK])
+        want = (float(codes[row, pos]) - 1.0) * d * xs[:, pos]   # exact in f64
+        want32 = want.astype(np.float32)                          # one rounding (exact on the MFMA path)
+        assert np.array_equal(y[:, row], want32), f"single-code row {row}: {y[:4, row]} vs {want32[:4]}"
+
+
+@pytest.mark.parametrize("label,path,ms,n,k", CASES, ids=[c[0] for c in CASES])
+def test_edge_weights_on_every_kernel(torch, label, path, ms, n, k):
+    aos, codes, bits = wl.edge_weight(n, k, seed=n + k)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for m in ms:
+            x = _x(m, k, seed=m + 7 * k)
+            note(f"[edge] {label}: M={m} N={n} K={k} {path}")
+            y = run_tq2(w, x, path)
+            assert not np.isnan(y).any(), "unwritten outputs"
+            y64, b = oracle.gemm(aos, n, k, x)
+            assert_within(y, y64, b, F32_REL if path == "f32" else MFMA_REL, f"edge {label} M={m}")
+            _exact_rows(y, x, codes, bits, path)
+    finally:
+        w.close()
+
+
+def test_edge_weights_decode_bit_exact(torch):
+    """The GPU decode of the edge weight, bit for bit (sign of zero included)."""
+    n, k = 1000, 1536
+    aos, _, _ = wl.edge_weight(n, k, seed=3)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        out = bw.tq2_dequant(w)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+    finally:
+        w.close()
+    assert np.array_equal(got.view(np.uint32), oracle.dequant(aos, n, k).view(np.uint32))
+
+
+def test_small_magnitude_x_in_the_f16_normal_range(torch):
+    """x ~ 1e-3 N(0, 1) (a few values fall below the f16 normal range): the MFMA path
+    still meets its bound; every output on both paths, on the tiled and skinny kernels."""
+    n, k = 1000, 4096
+    aos, _, _ = wl.edge_weight(n, k, seed=11)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for m, path in ((8, "mfma"), (40, "mfma"), (200, "mfma"), (1, "f32"), (3, "f32")):
+            x = (np.random.default_rng(m).standard_normal((m, k)) * 1e-3).astype(np.float32)
+            note(f"[edge] small x M={m} {path}")
+            y = run_tq2(w, x, path)
+            y64, b = oracle.gemm(aos, n, k, x)
+            assert_within(y, y64, b, F32_REL if path == "f32" else MFMA_REL, f"small x M={m} {path}")
+    finally:
+        w.close()
+
+
+def test_prefill_full(torch):
+    """Every one of the 8.4 M outputs of the 2048 x 4096 x 4096 prefill, both paths."""
+    aos, x = wl.prefill_inputs()
+    n = k = 4096
+    y64, b = oracle.gemm(aos, n, k, x)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for path in ("mfma", "f32"):
+            note(f"[prefill full] M=2048 N=4096 K=4096 {path}")
+            y = run_tq2(w, x, path)
+            assert not np.isnan(y).any()
+            assert_within(y, y64, b, F32_REL if path == "f32" else MFMA_REL, f"prefill full {path}")
+    finally:
+        w.close()
+
+
+def test_dit_small_shape_full(torch):
+    """The DiT 1536 x 3072 x 3072 benchmark shape ("oxibonsai-kernels 0.2.1 --
+    tests_gemm_tq2.rs", DiT benchmarks), every output, both paths."""
+    m, n, k = 1536, 3072, 3072
+    aos, x = wl.dit_weight(n, k), wl.dit_x(m, k)
+    y64, b = oracle.gemm(aos, n, k, x)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for path in ("mfma", "f32"):
+            note(f"[DiT full] {m}x{n}x{k} {path}")
+            y = run_tq2(w, x, path)
+            assert_within(y, y64, b, F32_REL if path == "f32" else MFMA_REL, f"DiT full {path}")
+    finally:
+        w.close()

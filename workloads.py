@@ -168,6 +168,52 @@ def dit_x(m: int, k: int) -> np.ndarray:
     return (i.astype(np.float32) * np.float32(0.001) - np.float32(0.12)).reshape(m, k).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------- edge cases of the format
+
+EDGE_CLASSES = 8  # row n of an edge weight belongs to class n % 8
+
+
+def edge_weight(n: int, k: int, seed: int):
+    """A weight exercising the block format's edge cases, row by row.
+
+    Row n has class n % 8:
+      0  every code 1 (byte 0x55): the weight is zero whatever the scale;
+      1  every code 1 except one code 0 or 2 at a random position;
+      2  every code 0 (byte 0x00): every weight is -d;
+      3  codes 0..3, every scale an f16 subnormal of either sign;
+      4  codes 0..3, every scale with 16384 <= |d| <= 32752 (2d still finite in f16), either sign;
+      5  codes 0..3, every scale negative (normal range);
+      6  codes 2 and 3 only;
+      7  codes 0..3, each block's scale drawn from {+-0, subnormal, normal, large}.
+    Other rows' scales are normal f16 values of either sign with |d| <= 32752.
+    Returns (aos bytes, codes [n][k] u8, scale bits [n][k/128] u16).
+    """
+    rng = np.random.default_rng(seed)
+    kb = k // BLOCK
+    codes = rng.integers(0, 4, (n, k), dtype=np.uint8)
+    sign = (rng.integers(0, 2, (n, kb)).astype(np.uint16) << np.uint16(15)).astype(np.uint16)
+    normal = rng.integers(0x0400, 0x7800, (n, kb)).astype(np.uint16)     # exponents 1..29: |d| <= 32752
+    subnormal = rng.integers(1, 0x0400, (n, kb)).astype(np.uint16)
+    large = rng.integers(0x7400, 0x7800, (n, kb)).astype(np.uint16)      # 16384 <= |d| <= 32752
+    cls = np.arange(n) % EDGE_CLASSES
+    bits = normal.copy()
+    codes[cls == 0] = 1
+    r1 = np.flatnonzero(cls == 1)
+    codes[r1] = 1
+    codes[r1, rng.integers(0, k, r1.size)] = rng.choice(np.array([0, 2], np.uint8), r1.size)
+    codes[cls == 2] = 0
+    bits[cls == 3] = subnormal[cls == 3]
+    bits[cls == 4] = large[cls == 4]
+    sign[cls == 5] = 0x8000
+    r6 = cls == 6
+    codes[r6] = rng.integers(2, 4, (int(r6.sum()), k), dtype=np.uint8)
+    kind = rng.integers(0, 4, (n, kb))
+    mixed = np.where(kind == 0, np.uint16(0), np.where(kind == 1, subnormal, np.where(kind == 2, normal, large)))
+    bits[cls == 7] = mixed[cls == 7]
+    bits = (bits | sign).astype(np.uint16)
+    return pack_tq2_aos(codes, bits), codes, bits
+
+
 # Seeded distribution workloads (index i: 1 decode, 2 MLP, 3 prefill, 4 BLR).
 DECODE = dict(name="decode_gemv", M=1, N=4096, K=4096, index=1)
 MLP = dict(name="mlp_up", Ms=(8, 32), N=14336, K=4096, index=2)
