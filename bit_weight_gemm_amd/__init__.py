@@ -27,7 +27,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq2.so")
 
-TQ2_OK, TQ2_EINVAL, TQ2_ENOMEM, TQ2_EDEVICE, TQ2_ENODEV = 0, -1, -2, -3, -4
+TQ2_OK, TQ2_EINVAL, TQ2_ENOMEM, TQ2_EDEVICE, TQ2_ENODEV, TQ2_ETOOBIG = 0, -1, -2, -3, -4, -5
+TQ2_STATIC_SCRATCH_BYTES = 16 << 20
 TQ2_PATH_AUTO, TQ2_PATH_F32, TQ2_PATH_MFMA = 0, 1, 2
 
 _lib = None
@@ -77,6 +78,7 @@ def lib():
         "blr_workspace_size": ([i64, i64, i64, i64], sz),
         "blr_forward": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p], i32),
         "blr_forward_paths": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p], i32),
+        "blr_forward_noalloc": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p], i32),
         "blr_forward_ws": ([p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
         "blr_forward_paths_ws": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
         "blr_backward_workspace_size": ([i64, i64, i64, i64], sz),

@@ -16,6 +16,13 @@
 
 using tq2::DevWeight;
 
+// Scratch of blr_forward_noalloc: a fixed device array of the library, one copy
+// per GPU, held from module load until the process ends.  Host code never uses
+// this name as an address: each device's copy is found once with
+// hipGetSymbolAddress (scratch_address below) and that pointer is what kernels
+// receive.
+static __device__ __align__(256) unsigned char scratch[TQ2_STATIC_SCRATCH_BYTES];
+
 struct tq2_weight {
     DevWeight dev;
     int device = -1;
@@ -138,6 +145,26 @@ int pool_reserve(Pool &p, size_t need) {
     return TQ2_OK;
 }
 
+// Device address of `scratch` on device `dev`, which must be the current device:
+// looked up with hipGetSymbolAddress on the first call made on that device and
+// kept (each GPU holds its own copy of the array, at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+int scratch_address(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return TQ2_ENODEV;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return TQ2_EDEVICE;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return TQ2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,6 +176,7 @@ const char *tq2_strerror(int status) {
         case TQ2_ENOMEM: return "out of memory";
         case TQ2_EDEVICE: return "HIP call or kernel launch failed";
         case TQ2_ENODEV: return "no gfx950 HIP device current";
+        case TQ2_ETOOBIG: return "the call needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -474,6 +502,25 @@ int blr_forward_paths(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v,
 int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
                 const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r, void *stream) {
     return blr_forward_paths(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, stream);
+}
+
+int blr_forward_noalloc(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                        const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
+                        void *stream) {
+    const size_t need = blr_workspace_size(M, d_in, d_out, r);
+    if (need == 0) return TQ2_EINVAL;
+    if (need > (size_t)TQ2_STATIC_SCRATCH_BYTES) return TQ2_ETOOBIG;  // sizes first: nothing else is looked at
+    int st = blr_forward_check(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    void *ws = nullptr;
+    st = scratch_address(dev, &ws);
+    if (st) return st;
+    // every byte of the workspace that the launches read, they first write: no clearing needed
+    return blr_forward_launch(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, ws,
+                              static_cast<hipStream_t>(stream));
 }
 
 int blr_backward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,

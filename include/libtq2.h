@@ -48,7 +48,11 @@ enum {
     TQ2_ENOMEM = -2,      /* device or host allocation failed */
     TQ2_EDEVICE = -3,     /* a HIP call or kernel launch failed */
     TQ2_ENODEV = -4,      /* no HIP device, or the current device is not gfx950 */
+    TQ2_ETOOBIG = -5,     /* blr_forward_noalloc: the sizes need more than its static scratch */
 };
+
+/* Bytes of the fixed device scratch array that blr_forward_noalloc uses (per GPU). */
+#define TQ2_STATIC_SCRATCH_BYTES (16u << 20)
 
 enum {
     TQ2_PATH_AUTO = 0,    /* choose by M (see tq2_select_path) */
@@ -131,6 +135,20 @@ int tq2_dequant(const tq2_weight *w, float *w_out, void *stream);
 int blr_forward(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                 const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
                 int64_t r, void *stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Computes exactly what
+ * blr_forward computes (the same kernels, so the same bits), with its workspace
+ * in a fixed device array of TQ2_STATIC_SCRATCH_BYTES (16 MiB) that the library
+ * holds on each GPU it runs on from module load until the process ends; the call
+ * itself allocates nothing.  Sizes whose workspace (blr_workspace_size) exceeds
+ * that array return TQ2_ETOOBIG before anything is queued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and give wrong results; serialise them.  Nothing in
+ * the array needs clearing between calls (each launch writes what it reads). */
+int blr_forward_noalloc(const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                        const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
+                        int64_t r, void *stream);
 
 /* [BLR] A layer of P paths, y = sum_p h_p . c_p, each path the product of
  * blr_forward with its own bitmaps and vectors (all paths share M, d_in, d_out
