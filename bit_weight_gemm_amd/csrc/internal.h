@@ -51,22 +51,20 @@ constexpr size_t kSkinnyMaxLds = 160 * 1024;  // all of gfx950's LDS per workgro
 bool skinny_fits(const DevWeight &w, int64_t M);
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s);
 
-// Binary low-rank forward.  Workspace carve-up is computed by blr_plan.
+// Binary low-rank forward.  Workspace carve-up is computed by blr_plan: the
+// f16 operand f16(l.a) [M][kpad2] that GEMM1 writes and GEMM2 reads.
 struct BlrPlan {
     int64_t M, d_in, d_out, r;
     int64_t kpad1, kpad2;        // contraction lengths of GEMM1 (d_in, padded) and GEMM2 (r, padded)
-    int64_t npad1, npad2;        // padded output widths of GEMM1 (r) and GEMM2 (d_out)
-    size_t off_codes_v, off_codes_u, off_al, off_xg, total;
+    size_t off_al, total;
 };
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 // Binary low-rank backward: the forward's carve-up, then the backward's buffers.
 struct BlrBwdPlan {
     BlrPlan fwd;
     int64_t kpado;               // d_out padded: contraction length of db = (dy.h) S_U
-    int64_t npadi;               // d_in padded: rows of S_V as the B operand of dx'
     int64_t chunks;              // token chunks of the column sums
-    size_t off_codes_ut, off_codes_vt, off_a, off_c, off_dyh, off_db, off_dbl, off_dxp, off_part_dh, off_part_dl, off_part_dg,
-        total;
+    size_t off_a, off_c, off_dyh, off_db, off_dbl, off_dxp, off_part_dh, off_part_dl, off_part_dg, total;
 };
 BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 // dh, dl, dg accumulate; dx is overwritten (accumulate_dx: dx = f32(dx + f32(g.dx')))

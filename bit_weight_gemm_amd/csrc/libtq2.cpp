@@ -343,7 +343,8 @@ size_t blr_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     if (M > ((int64_t)1 << 31) - 1 || d_in > ((int64_t)1 << 30) || d_out > ((int64_t)1 << 30) ||
         r > ((int64_t)1 << 30))
         return 0;
-    return tq2::blr_plan(M, d_in, d_out, r).total;
+    const size_t total = tq2::blr_plan(M, d_in, d_out, r).total;
+    return total > 256 ? total : 256;  // 0 means bad sizes: valid ones get at least one 256-byte unit
 }
 
 size_t blr_backward_workspace_size(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
@@ -357,13 +358,21 @@ uint64_t tq2_workspace_allocs(void) { return g_ws_allocs.load(); }
 
 namespace {
 
+// The kernels read each path's sign bitmaps with 32-bit byte offsets: each, with
+// the 512 rows of padding its products may step past its end, under 2 GB.
+bool bitmaps_fit(int64_t d_in, int64_t d_out, int64_t r) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (d_in + 512) * (r / 32) * 4 < lim && (d_out + 512) * (r / 32) * 4 < lim;
+}
+
 // Host-side checks of a BLR forward: P stacked paths of the given sizes, every
 // pointer and alignment, and y overlapping none of the inputs.  The workspace is
 // checked by the caller (it may be the library's own).
 int blr_forward_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                       const float *g, const float *x, const float *y, int64_t M, int64_t d_in, int64_t d_out,
                       int64_t r) {
-    if (blr_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096) return TQ2_EINVAL;
+    if (blr_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || !bitmaps_fit(d_in, d_out, r))
+        return TQ2_EINVAL;
     if (M == 0) return TQ2_OK;
     if (!bits_u || !bits_v || !h || !l || !g || !x || !y) return TQ2_EINVAL;
     if (!aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(bits_u) & 3u) ||
@@ -404,7 +413,8 @@ int blr_backward_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v
                        const float *g, const float *x, const float *dy, const float *dx, const float *dh,
                        const float *dl, const float *dg, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
                        float gscale) {
-    if (blr_backward_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16)
+    if (blr_backward_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16 ||
+        !bitmaps_fit(d_in, d_out, r))
         return TQ2_EINVAL;  // token chunks fit grid.y
     int e2 = 0;
     if (!std::isfinite(gscale) || gscale <= 0.0f || std::frexp(gscale, &e2) != 0.5f || gscale > 65536.0f)
@@ -508,7 +518,7 @@ int blr_forward_noalloc(const uint32_t *bits_u, const uint32_t *bits_v, const fl
                         const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
                         void *stream) {
     const size_t need = blr_workspace_size(M, d_in, d_out, r);
-    if (need == 0) return TQ2_EINVAL;
+    if (need == 0 || !bitmaps_fit(d_in, d_out, r)) return TQ2_EINVAL;
     if (need > (size_t)TQ2_STATIC_SCRATCH_BYTES) return TQ2_ETOOBIG;  // sizes first: nothing else is looked at
     int st = blr_forward_check(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r);
     if (st) return st;

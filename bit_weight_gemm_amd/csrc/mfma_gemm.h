@@ -8,8 +8,11 @@
 //    code-1 is in {-1,0,1,2} and d is an f16 (the page's simdgroup v10 kernel
 //    stages the weight tile the same way);
 //  * both products of the binary low-rank forward ("cortiq-engine 0.8.43 --
-//    train_mm.rs", mm_bits): A = f16(x.g) or f16(a.l), B = the sign bitmap
-//    re-laid as codes 0/2 (= -1/+1), no scale.
+//    train_mm.rs", mm_bits, which expands the sign bitmaps inside the GEMM):
+//    A = f16(x.g) (staged here from f32 x and g) or f16(a.l), B = the sign
+//    bitmap as the caller holds it, expanded to exact f16 +-1 in registers:
+//    bits along K are read as they are (kBSign); bits along N (the contraction
+//    runs down the bitmap's rows) are transposed in the LDS staging (kBSignT).
 //
 // Tiling: a workgroup of WM x WN x WK waves computes a BM x BN tile.  K is
 // walked in steps of 64*WK*KSUB; k group wk (WM x WN waves) takes KSUB 64-wide
@@ -49,12 +52,26 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc = 3, kEpiScale = 4, kEpiStoreHalf = 5,
            kEpiStoreNT = 6 };
 
+// B operand: kBCodes, 2-bit ternary codes in the device weight layout (with
+// optional scales); kBSign, a sign bitmap bits[n][ldb] with bit k%32 of word k/32
+// for element (n, k), set = +1; kBSignT, a sign bitmap bits[k][ldb] with bit n%32
+// of word n/32 for element (n, k) (the contraction runs down its rows).  The sign
+// modes need the A operand's k order permuted within groups (perm32 for kBSign,
+// perm4 for kBSignT, see decode.h): each A producer writes that order.
+enum BMode { kBCodes = 0, kBSign = 1, kBSignT = 2 };
+
 struct GemmArgs {
     const float *A;          // [M][lda] f32 (kAHalf: f16, read through Ah)
     const _Float16 *Ah;      // [M][lda] f16 (kAHalf)
     int64_t lda;
-    const uint32_t *codes;   // [Npad][kw] code words of B
+    const uint32_t *codes;   // [Npad][kw] code words of B (kBCodes)
     int64_t kw;
+    const uint32_t *bits;    // sign bitmap (kBSign: [nbits][ldb]; kBSignT: [kbits][ldb])
+    int64_t ldb;             // its words per row
+    int nbits, kbits;        // the bitmap's N and K extents: kBSign rows (N) and words per row (K);
+                             // kBSignT words per row (N) and rows (K); loads past them are clamped (the
+                             // results there are never stored, or meet zeros of A)
+    const float *g;          // kAXG/kAXGS: factor per k of A
     const uint16_t *scales;  // [Npad][kbw] f16 scales of B, or nullptr
     int64_t kbw;
     float *C;                // [M][ldc]
@@ -95,13 +112,28 @@ __device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15);
 // without a memory request ((rows of the last tile)*lda*4 < 2^31).  kAHalf: A already
 // rounded to f16, K a multiple of the step (zero-padded by the producer), rows
 // past M read row M-1.  Rows past M only reach output rows that are never stored.
-enum AMode { kAExact = 0, kABuf = 3, kAHalf = 4 };
+//
+// kAHalfBuf: as kAHalf, through a buffer resource ((M + BM)*lda*2 < 2^31).
+//
+// kAXG: A = f16(x[m][k] * g[k]) from f32 x and g, the product rounded to f32
+// and then to f16 (round to nearest even), stored in the perm4 k order of
+// kBSignT; x is read through a buffer resource, so K must be a multiple of the
+// step (no tail), rows 16-byte aligned and (M + BM)*lda*4 < 2^31.  kAXGS: the same
+// from scalar loads with 64-bit addresses, for any K (pieces past K read as
+// zero), alignment and size.
+enum AMode { kAExact = 0, kABuf = 3, kAHalf = 4, kAXG = 5, kAXGS = 6, kAHalfBuf = 7 };
 
 // Workgroup: WK groups of WM x WN waves.  Each step covers SK = 64*WK of K; wave
 // group wk takes the 64-wide slice wk of every step, and the groups' partial
 // tiles are added through LDS at the end (wk = 0, 1, ... in order).
+//
+// Epilogues kEpiHalfScaleP and kEpiStoreHalfP are kEpiHalfScale and
+// kEpiStoreHalf with the f16 output written in the perm32 k order, as the A
+// operand of a later kBSign product.
+constexpr int kEpiHalfScaleP = 7, kEpiStoreHalfP = 8;
+
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool SCALED,
-          int EPI, int ASTG, int KSUB>
+          int EPI, int ASTG, int KSUB, int BMODE>
 __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) {
     constexpr int NW = WM * WN;  // waves per k group
     constexpr int T = NW * WK * 64;
@@ -114,15 +146,28 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(STAGES >= 2, "at least two pipeline stages");
     static_assert(BDEPTH >= STAGES && BDEPTH % STAGES == 0, "B runs at least as far ahead as A");
-    static_assert(ASTG >= 1 && ASTG <= STAGES && BDEPTH % ASTG == 0, "A register stages");
+    static_assert(ASTG >= 1 && BDEPTH % ASTG == 0, "A register stages");
+    static_assert(BMODE == kBCodes || !SCALED, "sign bitmaps carry no scales");
+    static_assert(BMODE != kBSignT || AMODE == kAXG || AMODE == kAXGS || AMODE == kAHalf || AMODE == kAHalfBuf,
+                  "kBSignT needs A in the perm4 k order (kAXG, kAXGS, or a producer's f16)");
     // k-group sums go through the A tiles' LDS in RED_ROUNDS rounds, each taking
     // an equal share of the wave's MB x NB accumulator blocks
     constexpr int RED_ROUNDS = WK == 1 ? 1 : ((WK - 1) * BM * BN * 4 + STAGES * BM * SK * 2 - 1) / (STAGES * BM * SK * 2);
     static_assert((MB * NB) % RED_ROUNDS == 0, "k-group sums must split evenly over the rounds");
 
+    // B in LDS, per mode.  kBCodes: [slice][row slot][4 code words].  kBSign:
+    // [row][SROW words], the SK/32 bitmap words of the step (the 2-word pad keeps
+    // the 8-byte fragment reads of 32 rows on distinct banks).  kBSignT:
+    // [byte column c][k] bytes, byte c of contraction rows k (columns 8c..8c+7),
+    // TSTRIDE bytes per column (the 64-byte pad keeps the 4-byte stores of 16 row
+    // quads and 4 columns, and the 8-byte fragment reads, on distinct banks).
+    constexpr int SW = SK / 32, SROW = SW + 2;
+    constexpr int TW = BN / 32, TSTRIDE = SK + 64;
+    static_assert(BMODE != kBSignT || BN % 32 == 0, "kBSignT tiles hold whole bitmap words");
+    constexpr int BSM_WORDS = BMODE == kBCodes ? NSL * BN * 4 : BMODE == kBSign ? BN * SROW : (BN / 8) * TSTRIDE / 4;
     __shared__ __attribute__((aligned(16))) _Float16 As[STAGES][BM * SK];
-    __shared__ __attribute__((aligned(16))) uint32_t Bs[STAGES][NSL][BN * 4];  // 4 code words per row and slice
-    __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][NBLK][BN];     // B row scales of the step
+    __shared__ __attribute__((aligned(16))) uint32_t Bsm[STAGES][BSM_WORDS];
+    __shared__ __attribute__((aligned(8))) _Float16 Ds[STAGES][BMODE == kBCodes ? NBLK : 1][BN];  // B row scales
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wk = wave / NW, wr = wave % NW;
@@ -146,38 +191,70 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int j = 0; j < NB; ++j) acc[i][j] = f16x{};
 
     // Register stages of prefetch (see the pipeline below): STAGES for A, BDEPTH
-    // for B.  Every loaded value (A as f16, B code words and scales) goes through
-    // LDS, so a stage's registers are free again right after its LDS store.  B
-    // (the weight stream) may run further ahead than A (which other workgroups
-    // share through L2), to keep enough HBM reads in flight when the tiles are
-    // few.
-    // B arrives in 16-byte units holding one 16-element group of four rows; a
-    // step needs BN*WK units (BN/4 row quads x 4*WK groups), BPT per thread.
-    // When there are fewer units than threads, thread t takes unit t % BITEMS
-    // (duplicates load and store the same values), keeping the loop free of
-    // branches; the 8-byte scale units (one row quad, one block) likewise.
+    // for B.  Every loaded value (A as f16, B code words, bitmap words and
+    // scales) goes through LDS, so a stage's registers are free again right
+    // after its LDS store.  B (the weight stream) may run further ahead than A
+    // (which other workgroups share through L2), to keep enough HBM reads in
+    // flight when the tiles are few.
+    // kBCodes: B arrives in 16-byte units holding one 16-element group of four
+    // rows; a step needs BN*WK units (BN/4 row quads x 4*WK groups), BPT per
+    // thread.  When there are fewer units than threads, thread t takes unit
+    // t % BITEMS (duplicates load and store the same values), keeping the loop
+    // free of branches; the 8-byte scale units (one row quad, one block) likewise.
     constexpr int BITEMS = BN * NSL;
-    constexpr int BPT = (BITEMS + T - 1) / T;
-    static_assert(BITEMS % T == 0 || BITEMS < T, "B units: a multiple of the threads, or fewer");
+    constexpr int BPT = BMODE == kBCodes ? (BITEMS + T - 1) / T : 1;
+    static_assert(BMODE != kBCodes || BITEMS % T == 0 || BITEMS < T, "B units: a multiple of the threads, or fewer");
     constexpr int DITEMS = (BN / 4) * NBLK;
-    static_assert(DITEMS <= T && T % DITEMS == 0, "scale units must tile the threads");
+    static_assert(BMODE != kBCodes || (DITEMS <= T && T % DITEMS == 0), "scale units must tile the threads");
+    // kBSign: one bitmap word per item (row, word of the step), SPT per thread,
+    // duplicates as above.  kBSignT: thread t takes contraction row t (+T, ...) of
+    // the step and loads its TW words; lanes 4q..4q+3 hold rows 4q..4q+3, which a
+    // byte transpose across the quad turns into the [c][k] layout.
+    constexpr int SITEMS = BN * SW;
+    constexpr int SPT = BMODE == kBSign ? (SITEMS + T - 1) / T : 1;
+    static_assert(BMODE != kBSign || SITEMS % T == 0 || SITEMS < T, "bitmap words: a multiple of the threads, or fewer");
+    constexpr int TRPT = BMODE == kBSignT ? (SK + T - 1) / T : 1;  // contraction rows per thread
+    static_assert(BMODE != kBSignT || SK % T == 0 || (SK < T && SK % 64 == 0), "bitmap rows must tile the waves");
     // A is moved in 16-byte pieces (4 floats, or 8 halves for kAHalf): piece q
     // of tile row r covers k = EPP*q .. EPP*q+EPP-1 of the step; consecutive
     // lanes take consecutive pieces of a row, so each wave-wide load reads whole
     // row segments.
-    constexpr int EPP = AMODE == kAHalf ? 8 : 4;  // elements per piece
+    constexpr bool AXG = AMODE == kAXG || AMODE == kAXGS;
+    constexpr bool AH = AMODE == kAHalf || AMODE == kAHalfBuf;
+    constexpr int EPP = AH ? 8 : 4;  // elements per piece
     constexpr int QPR = SK / EPP;                  // pieces per row
     constexpr int PIECES = BM * QPR;
     constexpr int PPT = PIECES / T;
     static_assert(PIECES % T == 0, "A tile must split evenly over the threads");
+    static_assert(!AXG || T % QPR == 0, "kAXG: each thread's pieces share one k range (one g load per step)");
     f4 areg[ASTG][PPT];
-    u4 breg[BDEPTH][BPT];
-    uint2 dreg[BDEPTH];  // scales of one row quad and block
+    f4 greg[AXG ? ASTG : 1];
+    u4 breg[BMODE == kBCodes ? BDEPTH : 1][BPT];
+    uint2 dreg[BMODE == kBCodes ? BDEPTH : 1];  // scales of one row quad and block
+    uint32_t sreg[BMODE == kBSign ? BDEPTH : 1][SPT];
+    uint32_t treg[BMODE == kBSignT ? BDEPTH : 1][TRPT][TW];
 
-    // (only kABuf reads through it; unused otherwise)
-    const int64_t abytes = (int64_t)p.M * p.lda * 4;
+    // Buffer resources (32-bit offsets; a load past the range returns zero
+    // without a memory request): A of kABuf / kAXG (f32) and kAHalfBuf (f16)
+    // over its M rows, and the sign bitmap over its rows.
+    const int64_t abytes = (int64_t)p.M * p.lda * (AH ? 2 : 4);
+    const void *abase = AH ? static_cast<const void *>(p.Ah) : static_cast<const void *>(p.A);
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.A), (short)0, abytes < 0x7fffffff ? (int)abytes : 0x7fffffff, 0x00020000);
+        const_cast<void *>(abase), (short)0, abytes < 0x7fffffff ? (int)abytes : 0x7fffffff, 0x00020000);
+    const int64_t bbytes = (int64_t)(BMODE == kBSign ? p.nbits : p.kbits) * p.ldb * 4;
+    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(p.bits), (short)0, bbytes < 0x7fffffff ? (int)bbytes : 0x7fffffff, 0x00020000);
+    // element offset of each of this thread's pieces at k = 0 (gm*lda + q*EPP):
+    // fixed for the whole loop, so the buffer-resource modes add k0 only
+    constexpr bool ABUF = AMODE == kABuf || AMODE == kAXG || AMODE == kAHalfBuf;
+    int aoff[ABUF ? PPT : 1];
+    if constexpr (ABUF) {
+#pragma unroll
+        for (int c = 0; c < PPT; ++c) {
+            const int piece = tid + c * T;
+            aoff[c] = (m0 + piece / QPR) * (int)p.lda + (piece % QPR) * EPP;
+        }
+    }
     auto load_a = [&](int st, int k0) {
 #pragma unroll
         for (int c = 0; c < PPT; ++c) {
@@ -188,27 +265,71 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int gmc = gm < p.M ? gm : p.M - 1;
             if constexpr (AMODE == kAHalf) {
                 areg[st][c] = *reinterpret_cast<const f4 *>(p.Ah + (int64_t)gmc * p.lda + gk);  // 8 halves
-            } else if constexpr (AMODE == kABuf) {
-                areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (gm * (int)p.lda + gk) * 4, 0, 0));
+            } else if constexpr (AMODE == kAHalfBuf) {
+                areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (aoff[c] + k0) * 2, 0, 0));
+            } else if constexpr (AMODE == kABuf || AMODE == kAXG) {
+                areg[st][c] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, (aoff[c] + k0) * 4, 0, 0));
+            } else if constexpr (AMODE == kAXGS) {
+                const float *xr = p.A + (int64_t)gmc * p.lda;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) areg[st][c][e] = gk + e < p.K ? xr[gk + e] : 0.0f;
             } else {
                 static_assert(AMODE == kAExact, "A mode");
                 areg[st][c] = *reinterpret_cast<const f4 *>(p.A + (int64_t)gmc * p.lda + gk);
             }
         }
-    };
-    auto load_b = [&](int st, int k0) {
-        const u4 *c4 = reinterpret_cast<const u4 *>(p.codes);
+        if constexpr (AXG) {  // the k range of this thread's pieces (the same for every c)
+            const int gk = k0 + (tid % QPR) * EPP;
+            if constexpr (AMODE == kAXG) {
+                greg[st] = *reinterpret_cast<const f4 *>(p.g + gk);  // no K tail in this mode
+            } else {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int item = (tid + i * T) % BITEMS;
-            const int64_t quad = (n0 >> 2) + item / (4 * NSL);
-            breg[st][i] = c4[quad * p.kw + (k0 >> 4) + item % (4 * NSL)];
+                for (int e = 0; e < 4; ++e) greg[st][e] = gk + e < p.K ? p.g[gk + e] : 0.0f;
+            }
         }
-        // whole waves past DITEMS skip the scales (a wave-uniform branch)
-        if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
-            const uint2 *s4 = reinterpret_cast<const uint2 *>(p.scales);
-            const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
-            dreg[st] = s4[((n0 >> 2) + quad) * p.kbw + k0 / kBlock + blk];
+    };
+    // word offset of each bitmap item at k = 0 (kBSign: row (n0 + row), word w)
+    int soff[SPT];
+    if constexpr (BMODE == kBSign) {
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int item = (tid + i * T) % SITEMS;
+            soff[i] = (n0 + item / SW) * (int)p.ldb + item % SW;
+        }
+    }
+    auto load_b = [&](int st, int k0) {
+        if constexpr (BMODE == kBCodes) {
+            const u4 *c4 = reinterpret_cast<const u4 *>(p.codes);
+#pragma unroll
+            for (int i = 0; i < BPT; ++i) {
+                const int item = (tid + i * T) % BITEMS;
+                const int64_t quad = (n0 >> 2) + item / (4 * NSL);
+                breg[st][i] = c4[quad * p.kw + (k0 >> 4) + item % (4 * NSL)];
+            }
+            // whole waves past DITEMS skip the scales (a wave-uniform branch)
+            if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
+                const uint2 *s4 = reinterpret_cast<const uint2 *>(p.scales);
+                const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
+                dreg[st] = s4[((n0 >> 2) + quad) * p.kbw + k0 / kBlock + blk];
+            }
+        } else if constexpr (BMODE == kBSign) {
+            // rows past N read zero (the buffer's range); words past the row's
+            // valid ones read the next row (finite signs that meet zeros of A)
+#pragma unroll
+            for (int i = 0; i < SPT; ++i) sreg[st][i] = __builtin_amdgcn_raw_buffer_load_b32(brsrc, (soff[i] + (k0 >> 5)) * 4, 0, 0);
+        } else {
+            // contraction rows past K read zero (they meet zeros of A); words past
+            // the row's valid ones read the next row (columns whose results are
+            // never stored, or are scaled by zero)
+            if (SK >= T || tid < SK) {  // wave-uniform
+#pragma unroll
+                for (int rr = 0; rr < TRPT; ++rr) {
+                    const int k = k0 + tid + rr * T;
+#pragma unroll
+                    for (int w = 0; w < TW; ++w)
+                        treg[st][rr][w] = __builtin_amdgcn_raw_buffer_load_b32(brsrc, (k * (int)p.ldb + (n0 >> 5) + w) * 4, 0, 0);
+                }
+            }
         }
     };
     // store(st, sa, sb): A register stage sa and B register stage sb into LDS buffer st
@@ -217,26 +338,66 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int c = 0; c < PPT; ++c) {
             const int piece = tid + c * T;
             const int row = piece / QPR, q = piece % QPR;
-            if constexpr (AMODE == kAHalf) {
+            if constexpr (AH) {
                 *reinterpret_cast<f4 *>(&As[st][lds_off<NCH>(row, q)]) = areg[sa][c];  // a whole 16-byte chunk
             } else {
                 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
                 h4 v;
+                if constexpr (AXG) {
+                    // f16(x*g): the product rounded to f32, then to f16; stored in
+                    // the perm4 order (k0, k2, k1, k3) that kBSignT's decode expects
+                    const f4 xg = areg[sa][c] * greg[sa];
+                    v = h4{(_Float16)xg[0], (_Float16)xg[2], (_Float16)xg[1], (_Float16)xg[3]};
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (_Float16)areg[sa][c][e];
+                    for (int e = 0; e < 4; ++e) v[e] = (_Float16)areg[sa][c][e];
+                }
                 *reinterpret_cast<h4 *>(&As[st][lds_off<NCH>(row, q >> 1) + ((q & 1) << 2)]) = v;
             }
         }
+        if constexpr (BMODE == kBCodes) {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int item = (tid + i * T) % BITEMS;
-            const int r0 = (item / (4 * NSL)) * 4, g = item % (4 * NSL);
+            for (int i = 0; i < BPT; ++i) {
+                const int item = (tid + i * T) % BITEMS;
+                const int r0 = (item / (4 * NSL)) * 4, g = item % (4 * NSL);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Bs[st][g >> 2][b_slot(r0 + r) * 4 + (g & 3)] = breg[sb][i][r];
-        }
-        if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
-            const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
-            *reinterpret_cast<uint2 *>(&Ds[st][blk][4 * quad]) = dreg[sb];
+                for (int r = 0; r < 4; ++r) Bsm[st][(g >> 2) * (BN * 4) + b_slot(r0 + r) * 4 + (g & 3)] = breg[sb][i][r];
+            }
+            if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
+                const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
+                *reinterpret_cast<uint2 *>(&Ds[st][blk][4 * quad]) = dreg[sb];
+            }
+        } else if constexpr (BMODE == kBSign) {
+#pragma unroll
+            for (int i = 0; i < SPT; ++i) {
+                const int item = (tid + i * T) % SITEMS;
+                Bsm[st][(item / SW) * SROW + item % SW] = sreg[sb][i];
+            }
+        } else {
+            // 4x4 byte transpose across each lane quad (rows 4q..4q+3 of the step,
+            // byte columns 4w..4w+3 of word w): two exchanges, with the partner
+            // two lanes away and then one lane away, each keeping half the bytes
+            // and taking the other half from the partner.  Lane i of the quad
+            // ends with byte column 4w+i of the four rows, one row per byte.
+            if (SK >= T || tid < SK) {
+                const int i = lane & 3;
+                const uint32_t sel2 = (i & 2) ? 0x03020706u : 0x05040100u;  // keep bytes 0,1 / take 2,3 (or the reverse)
+                const uint32_t sel1 = (i & 1) ? 0x03070105u : 0x06020400u;  // keep bytes 0,2 / take 1,3 (or the reverse)
+#pragma unroll
+                for (int rr = 0; rr < TRPT; ++rr) {
+                    const int k = tid + rr * T;  // contraction row of the step
+#pragma unroll
+                    for (int w = 0; w < TW; ++w) {
+                        const uint32_t b = treg[sb][rr][w];
+                        const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+                        const uint32_t b2 = __builtin_amdgcn_perm(p2, b, sel2);
+                        const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b2, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+                        const uint32_t col = __builtin_amdgcn_perm(p1, b2, sel1);
+                        *reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(&Bsm[st][0]) +
+                                                      (4 * w + i) * TSTRIDE + (k & ~3)) = col;
+                    }
+                }
+            }
         }
     };
 
@@ -248,12 +409,17 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int ks = 0; ks < KSUB; ++ks) {
             const int sl = wk * KSUB + ks;  // this wave's slice of the step
             u4 bw[NB];
+            uint2 sw2[NB];
             _Float16 dv[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int row = wn * WTN + nb * 32 + lrow;
-                bw[nb] = *reinterpret_cast<const u4 *>(&Bs[st][sl][b_slot(row) * 4]);
-                dv[nb] = SCALED ? Ds[st][(sl * BK) / kBlock][row] : (_Float16)1.0f;
+                if constexpr (BMODE == kBCodes) {
+                    bw[nb] = *reinterpret_cast<const u4 *>(&Bsm[st][sl * (BN * 4) + b_slot(row) * 4]);
+                    dv[nb] = SCALED ? Ds[st][(sl * BK) / kBlock][row] : (_Float16)1.0f;
+                } else if constexpr (BMODE == kBSign) {
+                    sw2[nb] = *reinterpret_cast<const uint2 *>(&Bsm[st][row * SROW + 2 * sl]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -265,8 +431,20 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    b[nb] = half_group_m1(bw[nb][j], hk, magic);
-                    if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
+                    if constexpr (BMODE == kBCodes) {
+                        b[nb] = half_group_m1(bw[nb][j], hk, magic);
+                        if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
+                    } else if constexpr (BMODE == kBSign) {
+                        // octet 2*(j&1)+hk of the slice's word j/2 (k order perm32)
+                        b[nb] = sign_octet(j < 2 ? sw2[nb].x : sw2[nb].y, 2 * (j & 1) + hk, magic);
+                    } else {
+                        // column n, contraction rows sl*64 + 16j + 8hk .. +7 (k order perm4)
+                        const int n = wn * WTN + nb * 32 + lrow;
+                        const uint2 v = *reinterpret_cast<const uint2 *>(
+                            reinterpret_cast<const unsigned char *>(&Bsm[st][0]) + (n >> 3) * TSTRIDE +
+                            sl * 64 + 16 * j + 8 * hk);
+                        b[nb] = sign_rows8(v.x, v.y, n & 7, magic);
+                    }
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
@@ -396,7 +574,11 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             if (gn >= p.N) continue;
             float rf = 1.0f;
             if constexpr (EPI == kEpiRowScale || EPI == kEpiRowScaleAcc) rf = p.rowf[gn];
-            if constexpr (EPI == kEpiHalfScale || EPI == kEpiStoreHalf) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
+            constexpr bool HALF_OUT = EPI == kEpiHalfScale || EPI == kEpiStoreHalf || EPI == kEpiHalfScaleP ||
+                                      EPI == kEpiStoreHalfP;
+            constexpr bool PERM_OUT = EPI == kEpiHalfScaleP || EPI == kEpiStoreHalfP;
+            if constexpr (HALF_OUT) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
+            const int hn = PERM_OUT ? perm32(gn) : gn;  // column of the f16 output
             if constexpr (EPI == kEpiScale) rf = p.alpha;
             float *C = p.C;
 #pragma unroll
@@ -404,11 +586,11 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (gm < p.M) {
                     const float v = acc[mb][nb][r];
-                    if constexpr (EPI == kEpiHalfScale) {
-                        p.Ch[(int64_t)gm * p.ldc + gn] = (_Float16)(rf * v);
-                    } else if constexpr (EPI == kEpiStoreHalf) {
+                    if constexpr (EPI == kEpiHalfScale || EPI == kEpiHalfScaleP) {
+                        p.Ch[(int64_t)gm * p.ldc + hn] = (_Float16)(rf * v);
+                    } else if constexpr (EPI == kEpiStoreHalf || EPI == kEpiStoreHalfP) {
                         if (gn < p.nrowf) C[(int64_t)gm * p.ldc + gn] = v;
-                        p.Ch[(int64_t)gm * p.ldch + gn] = (_Float16)(rf * v);
+                        p.Ch[(int64_t)gm * p.ldch + hn] = (_Float16)(rf * v);
                     } else if constexpr (EPI == kEpiRowScaleAcc) {
                         // two roundings: the product must not be fused into the sum
 #pragma clang fp contract(off)
@@ -425,12 +607,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 }
 
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool SCALED, int EPI,
-          int BDEPTH = STAGES, int ASTG = STAGES, int KSUB = 1>
+          int BDEPTH = STAGES, int ASTG = STAGES, int KSUB = 1, int BMODE = kBCodes>
 inline hipError_t run_gemm(GemmArgs p, hipStream_t s) {
-    p.tiles_n = (int)((p.N + BN - 1) / BN);  // tiles_n * BN <= Npad, so B rows stay in bounds
+    p.tiles_n = (int)((p.N + BN - 1) / BN);  // kBCodes: tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
     const int64_t tiles = tiles_m * p.tiles_n;
-    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, SCALED, EPI, ASTG, KSUB>
+    mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, SCALED, EPI, ASTG, KSUB, BMODE>
         <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();
 }

@@ -105,7 +105,7 @@ def test_workspace_counter_starts_at_zero_without_a_device(L):
 
 
 def test_workspace_size_rules(L):
-    assert bw.blr_workspace_size(512, 4096, 4096, 1024) > 512 * 1024 * 4
+    assert bw.blr_workspace_size(512, 4096, 4096, 1024) == 512 * 1024 * 2   # f16(l.a) [M][r]
     assert bw.blr_workspace_size(1, 4096, 4096, 1000) == 0     # r % 32 != 0
     assert bw.blr_workspace_size(1, 0, 4096, 1024) == 0        # d_in < 1
     assert bw.blr_workspace_size(-1, 8, 8, 32) == 0            # M < 0

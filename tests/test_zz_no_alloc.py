@@ -63,7 +63,7 @@ def test_noalloc_matches_blr_forward_on_two_calls(torch):
 
 
 def test_noalloc_refuses_sizes_beyond_its_scratch(torch):
-    m, d_in, d_out, r = 8192, 4096, 4096, 1024
+    m, d_in, d_out, r = 16384, 4096, 4096, 1024
     assert bw.blr_workspace_size(m, d_in, d_out, r) > bw.TQ2_STATIC_SCRATCH_BYTES
     # refused from the sizes alone, before any pointer or device is looked at
     st = bw.lib().blr_forward_noalloc(None, None, None, None, None, None, None, m, d_in, d_out, r, None)
