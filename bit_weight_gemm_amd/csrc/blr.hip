@@ -126,19 +126,23 @@ hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const u
 // product also keeps a in f32 for dl.
 // The two new products read the bitmaps in the other orientation: db contracts
 // over d_out, down the rows of bits_u (kBSignT, as GEMM1 reads bits_v), and dx'
-// over r, along the rows of bits_v (kBSign, as GEMM2 reads bits_u); their f16
-// inputs are written in the k order each decode expects (perm4 and perm32).
-// Column sums over the tokens go in two passes, chunks of kColChunk tokens then
-// the chunks in order, so results do not depend on timing; small chunks give
-// enough threads (columns x chunks) to keep the loads in flight.
+// over r, along the rows of bits_v (kBSign, as GEMM2 reads bits_u).  The column
+// sums over the tokens and the f16 staging of each next product's input are
+// done in the epilogues of the products that produce their operands (the
+// kEpiBwd* modes of mfma_gemm.h): c's epilogue reads dy and keeps the partial
+// sums of dy.c per block of 32 tokens and writes f16(dy.h.gs) (perm4 order, for
+// db); db's reads a, keeps those of a.db and writes f16(db.l.gs) (perm32 order,
+// for dx'); dx''s reads x, keeps those of x.dx' and writes dx.  A last launch
+// adds each gradient's partial sums, the blocks in order.  So c, db and dx'
+// never go to memory, and the backward is five launches.
 
-constexpr int kColChunk = 16;
+static int64_t row_blocks(int64_t M) { return (M + 31) / 32; }
 
 BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     BlrBwdPlan p{};
     p.fwd = blr_plan(M, d_in, d_out, r);
     p.kpado = round_up(d_out, kBlrKPad);
-    p.chunks = (M + kColChunk - 1) / kColChunk;
+    p.blocks = row_blocks(M);
     size_t off = p.fwd.total;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -146,118 +150,51 @@ BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
         return at;
     };
     p.off_a = take((size_t)M * r * 4);
-    p.off_c = take((size_t)M * d_out * 4);
     p.off_dyh = take((size_t)M * p.kpado * 2);
-    p.off_db = take((size_t)M * r * 4);
     p.off_dbl = take((size_t)M * p.fwd.kpad2 * 2);
-    p.off_dxp = take((size_t)M * d_in * 4);
-    const size_t ch = (size_t)(p.chunks > 0 ? p.chunks : 1);
-    p.off_part_dh = take(ch * d_out * 4);
-    p.off_part_dl = take(ch * r * 4);
-    p.off_part_dg = take(ch * d_in * 4);
+    const size_t nb = (size_t)(p.blocks > 0 ? p.blocks : 1);
+    p.off_part_dh = take(nb * d_out * 4);
+    p.off_part_dl = take(nb * r * 4);
+    p.off_part_dg = take(nb * d_in * 4);
     p.total = off;
     return p;
 }
 
 namespace {
 
-enum ColMode { kColStageH = 0, kColDx = 1, kColDxAcc = 2 };
-
-// Pass 2 of a column sum, for column n: out[n] = f32(out[n] + f32(sum over chunks
-// in order of part[ch][n])).  The loads of a group of chunks are independent:
-// issue them together, then add in order.
-__device__ __forceinline__ void column_finish(const float *__restrict__ part, float *__restrict__ out, int64_t N,
-                                              int64_t chunks, int64_t n) {
-    float s = 0.0f;
-    int64_t ch = 0;
-    for (; ch + 16 <= chunks; ch += 16) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = part[(ch + i) * N + n];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += v[i];
-    }
-    for (; ch < chunks; ++ch) s += part[ch * N + n];
-    out[n] = out[n] + s;
-}
-
-// Pass 1 of a column sum: part[ch][n] = sum over tokens t of chunk ch of
-// A[t][n] * B[t][n] (f32, ascending t), for n < N.  Fused with the elementwise
-// op that reads the same operand A:
-//   kColStageH: H[t][n'] = f16(A[t][n] * f[n] * gs) for n < N, 0 for N <= n < ldh,
-//               with n' = n, perm4(n) or perm32(n) (hperm 0, 4, 32): the k order of
-//               the product that reads H;
-//   kColDx:     D[t][n] = f[n] * B[t][n];
-//   kColDxAcc:  D[t][n] = f32(D[t][n] + f32(f[n] * B[t][n])).
-// Workgroups past the column blocks (chunk 0 only) run pass 2 of an earlier
-// column sum (fpart -> fout, fN columns, fchunks chunks), which saves it a launch
-// of its own; its partials are in a buffer of their own, so the two do not meet.
-struct ColArgs {
-    const float *A, *B, *f;
-    float *part;
-    _Float16 *H;
-    float *D;
-    int64_t M, N, lda, ldh;
-    int hperm;
-    float gs;
-    const float *fpart;  // earlier column sum to finish, or nullptr
-    float *fout;
-    int64_t fN, fchunks;
+// out[n] = f32(out[n] + f32(sum over row blocks b in order of part[b][n])) for the
+// three gradients of a path (dh: d_out columns, dl: r, dg: d_in), one thread per
+// column; the loads of a group of blocks are independent, so they go out
+// together, then are added in order.
+struct FinishJob {
+    const float *part;
+    float *out;
+    int64_t N;
+};
+struct FinishArgs {
+    FinishJob job[3];
+    int64_t blocks;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(256) void blr_colsum_kernel(ColArgs q) {
+__global__ __launch_bounds__(256) void blr_finish_kernel(FinishArgs q) {
 #pragma clang fp contract(off)
-    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
-    const int64_t cblocks = (ncols + 255) / 256;
-    if ((int64_t)blockIdx.x >= cblocks) {
-        const int64_t n = ((int64_t)blockIdx.x - cblocks) * 256 + threadIdx.x;
-        if (blockIdx.y == 0 && n < q.fN) column_finish(q.fpart, q.fout, q.fN, q.fchunks, n);
-        return;
+    int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int j = 0;
+    while (j < 3 && n >= q.job[j].N) n -= q.job[j++].N;
+    if (j == 3) return;
+    const float *__restrict__ part = q.job[j].part;
+    const int64_t N = q.job[j].N;
+    float s = 0.0f;
+    int64_t b = 0;
+    for (; b + 16 <= q.blocks; b += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = part[(b + i) * N + n];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = s + v[i];
     }
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t ch = blockIdx.y;
-    const int64_t t0 = ch * kColChunk, t1 = t0 + kColChunk < q.M ? t0 + kColChunk : q.M;
-    if (n >= ncols) return;
-    const int64_t hn = q.hperm == 4 ? perm4((int)n) : q.hperm == 32 ? perm32((int)n) : n;
-    if (n >= q.N) {  // padding columns of the staged operand
-        for (int64_t t = t0; t < t1; ++t) q.H[t * q.ldh + hn] = (_Float16)0.0f;
-        return;
-    }
-    const float *__restrict__ A = q.A;
-    const float *__restrict__ B = q.B;
-    _Float16 *__restrict__ H = q.H;
-    float *__restrict__ D = q.D;
-    const float f = q.f[n];
-    float sum = 0.0f;
-#pragma unroll 4
-    for (int64_t t = t0; t < t1; ++t) {
-        const float a = A[t * q.lda + n], b = B[t * q.lda + n];
-        sum = sum + a * b;  // product rounded before the sum (no contraction in this kernel)
-        if constexpr (MODE == kColStageH) H[t * q.ldh + hn] = (_Float16)(a * f * q.gs);
-        if constexpr (MODE == kColDx) D[t * q.lda + n] = f * b;
-        if constexpr (MODE == kColDxAcc) {
-            const float prod = f * b;
-            D[t * q.lda + n] = D[t * q.lda + n] + prod;
-        }
-    }
-    q.part[ch * q.N + n] = sum;
-}
-
-// Pass 2 alone (the last column sum of a path).
-__global__ __launch_bounds__(256) void blr_colsum_finish_kernel(const float *__restrict__ part, float *__restrict__ out,
-                                                                int64_t N, int64_t chunks) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n < N) column_finish(part, out, N, chunks, n);
-}
-
-// Pass 1 of q (and pass 2 of the column sum q.fpart names, if any).
-template <int MODE>
-hipError_t colsum_pass1(const ColArgs &q, int64_t chunks, hipStream_t s) {
-    const int64_t ncols = MODE == kColStageH ? q.ldh : q.N;
-    const int64_t fblocks = q.fpart ? (q.fN + 255) / 256 : 0;
-    blr_colsum_kernel<MODE><<<dim3((unsigned)((ncols + 255) / 256 + fblocks), (unsigned)chunks), dim3(256), 0, s>>>(q);
-    return hipGetLastError();
+    for (; b < q.blocks; ++b) s = s + part[b * N + n];
+    q.job[j].out[n] = q.job[j].out[n] + s;
 }
 
 }  // namespace
@@ -271,11 +208,8 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
     auto at = [&](size_t off) { return ws + off; };
     _Float16 *al = reinterpret_cast<_Float16 *>(at(pl.off_al));
     float *a = reinterpret_cast<float *>(at(pb.off_a));
-    float *c = reinterpret_cast<float *>(at(pb.off_c));
     _Float16 *dyh = reinterpret_cast<_Float16 *>(at(pb.off_dyh));
-    float *db = reinterpret_cast<float *>(at(pb.off_db));
     _Float16 *dbl = reinterpret_cast<_Float16 *>(at(pb.off_dbl));
-    float *dxp = reinterpret_cast<float *>(at(pb.off_dxp));
     float *part_dh = reinterpret_cast<float *>(at(pb.off_part_dh));
     float *part_dl = reinterpret_cast<float *>(at(pb.off_part_dl));
     float *part_dg = reinterpret_cast<float *>(at(pb.off_part_dg));
@@ -288,59 +222,48 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         e = run_gemm1<kEpiStoreHalfP>(p, pl, xg_vector(pl, x, g), s);
         if (e != hipSuccess) return e;
     }
-    // c = al . S_U^T   [M][d_out]
+    // c = al . S_U^T (not stored): partial sums of dy.c, and dyh = f16(dy.h.gs) [M][kpado] (perm4 order)
     {
         GemmArgs p = gemm2_args(pl, bits_u, al);
-        p.C = c, p.ldc = d_out;
-        e = gemm_short_k<kEpiStore>(p, s);
+        p.N = (int)pb.kpado, p.nrowf = (int)d_out, p.rowf = h;
+        p.ea = dy, p.ldea = d_out, p.part = part_dh, p.Ch = dyh, p.ldch = pb.kpado, p.gs = gs;
+        e = gemm_short_k<kEpiBwdC>(p, s);
         if (e != hipSuccess) return e;
     }
-    // dh += sum_t dy.c, with dyh = f16(dy.h.gs) (perm4 order, for db) staged from the same reads
-    {
-        ColArgs q{};
-        q.A = dy, q.B = c, q.f = h, q.part = part_dh, q.H = dyh, q.M = M, q.N = d_out, q.lda = d_out, q.ldh = pb.kpado;
-        q.hperm = 4, q.gs = gs;
-        e = colsum_pass1<kColStageH>(q, pb.chunks, s);
-        if (e != hipSuccess) return e;
-    }
-    // db = dyh . S_U / gs   [M][r]: contraction over d_out, down the rows of bits_u
+    // db = dyh . S_U / gs (not stored; contraction over d_out, down the rows of bits_u):
+    // partial sums of a.db, and dbl = f16(db.l.gs) [M][kpad2] (perm32 order)
     {
         GemmArgs p{};
         p.Ah = dyh, p.lda = pb.kpado;
         p.bits = bits_u, p.ldb = r / 32, p.nbits = (int)(r / 32), p.kbits = (int)d_out;
-        p.C = db, p.ldc = r, p.M = (int)M, p.N = (int)r, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
-        p.alpha = 1.0f / gs;
-        e = half_buf(p) ? gemm_long_k<kEpiScale, kAHalfBuf>(p, pb.kpado, small, s)
-                        : gemm_long_k<kEpiScale, kAHalf>(p, pb.kpado, small, s);
+        p.M = (int)M, p.N = (int)pl.kpad2, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
+        p.alpha = 1.0f / gs, p.nrowf = (int)r, p.rowf = l;
+        p.ea = a, p.ldea = r, p.part = part_dl, p.Ch = dbl, p.ldch = pl.kpad2, p.gs = gs;
+        e = half_buf(p) ? gemm_long_k<kEpiBwdDb, kAHalfBuf>(p, pb.kpado, small, s)
+                        : gemm_long_k<kEpiBwdDb, kAHalf>(p, pb.kpado, small, s);
         if (e != hipSuccess) return e;
     }
-    // dl += sum_t a.db, with dbl = f16(db.l.gs) (perm32 order, for dx') staged from the same reads
-    {
-        ColArgs q{};
-        q.A = db, q.B = a, q.f = l, q.part = part_dl, q.H = dbl, q.M = M, q.N = r, q.lda = r, q.ldh = pl.kpad2;
-        q.hperm = 32, q.gs = gs;
-        q.fpart = part_dh, q.fout = dh, q.fN = d_out, q.fchunks = pb.chunks;  // and dh's second pass
-        e = colsum_pass1<kColStageH>(q, pb.chunks, s);
-        if (e != hipSuccess) return e;
-    }
-    // dx' = dbl . S_V^T / gs   [M][d_in]: contraction over r, along the rows of bits_v
+    // dx' = dbl . S_V^T / gs (not stored; contraction over r, along the rows of bits_v):
+    // partial sums of x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
     {
         GemmArgs p{};
         p.Ah = dbl, p.lda = pl.kpad2;
         p.bits = bits_v, p.ldb = r / 32, p.nbits = (int)d_in, p.kbits = (int)(r / 32);
-        p.C = dxp, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
-        p.alpha = 1.0f / gs;
-        e = gemm_short_k<kEpiScale>(p, s);
+        p.C = dx, p.ldc = d_in, p.M = (int)M, p.N = (int)d_in, p.K = (int)pl.kpad2, p.Kloop = (int)pl.kpad2;
+        p.alpha = 1.0f / gs, p.nrowf = (int)d_in, p.rowf = g;
+        p.ea = x, p.ldea = d_in, p.part = part_dg;
+        e = accumulate_dx ? gemm_short_k<kEpiBwdDxAcc>(p, s) : gemm_short_k<kEpiBwdDx>(p, s);
         if (e != hipSuccess) return e;
     }
-    // dg += sum_t x.dx', and dx = g.dx' (later paths: dx = f32(dx + f32(g.dx')))
+    // dh, dl, dg += their partial sums, the row blocks in order
     {
-        ColArgs q{};
-        q.A = x, q.B = dxp, q.f = g, q.part = part_dg, q.D = dx, q.M = M, q.N = d_in, q.lda = d_in;
-        q.fpart = part_dl, q.fout = dl, q.fN = r, q.fchunks = pb.chunks;  // and dl's second pass
-        e = accumulate_dx ? colsum_pass1<kColDxAcc>(q, pb.chunks, s) : colsum_pass1<kColDx>(q, pb.chunks, s);
-        if (e != hipSuccess) return e;
-        blr_colsum_finish_kernel<<<dim3((unsigned)((d_in + 255) / 256)), dim3(256), 0, s>>>(part_dg, dg, d_in, pb.chunks);
+        FinishArgs q{};
+        q.job[0] = FinishJob{part_dh, dh, d_out};
+        q.job[1] = FinishJob{part_dl, dl, r};
+        q.job[2] = FinishJob{part_dg, dg, d_in};
+        q.blocks = pb.blocks;
+        const int64_t cols = d_out + r + d_in;
+        blr_finish_kernel<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s>>>(q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -63,8 +63,8 @@ BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 struct BlrBwdPlan {
     BlrPlan fwd;
     int64_t kpado;               // d_out padded: contraction length of db = (dy.h) S_U
-    int64_t chunks;              // token chunks of the column sums
-    size_t off_a, off_c, off_dyh, off_db, off_dbl, off_dxp, off_part_dh, off_part_dl, off_part_dg, total;
+    int64_t blocks;              // blocks of 32 tokens (rows of the column partial sums)
+    size_t off_a, off_dyh, off_dbl, off_part_dh, off_part_dl, off_part_dg, total;
 };
 BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 // dh, dl, dg accumulate; dx is overwritten (accumulate_dx: dx = f32(dx + f32(g.dx')))

@@ -413,9 +413,8 @@ int blr_backward_check(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v
                        const float *g, const float *x, const float *dy, const float *dx, const float *dh,
                        const float *dl, const float *dg, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
                        float gscale) {
-    if (blr_backward_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || M > (int64_t)65535 * 16 ||
-        !bitmaps_fit(d_in, d_out, r))
-        return TQ2_EINVAL;  // token chunks fit grid.y
+    if (blr_backward_workspace_size(M, d_in, d_out, r) == 0 || P < 1 || P > 4096 || !bitmaps_fit(d_in, d_out, r))
+        return TQ2_EINVAL;
     int e2 = 0;
     if (!std::isfinite(gscale) || gscale <= 0.0f || std::frexp(gscale, &e2) != 0.5f || gscale > 65536.0f)
         return TQ2_EINVAL;  // a power of two, at most 2^16

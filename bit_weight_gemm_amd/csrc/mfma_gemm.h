@@ -79,7 +79,11 @@ struct GemmArgs {
     int64_t ldc, ldch;
     const float *rowf;       // [N] output factor (kEpiRowScale, kEpiHalfScale)
     int nrowf;               // factors present (kEpiHalfScale: columns past it get 0)
-    float alpha;             // output factor (kEpiScale)
+    float alpha;             // output factor (kEpiScale, the backward epilogues)
+    const float *ea;         // backward epilogues: the elementwise operand E [M][ldea] (dy, a or x)
+    int64_t ldea;
+    float *part;             // backward epilogues: column partial sums [ceil(M/32)][nrowf]
+    float gs;                // backward epilogues: gradient scale of the f16 output
     int M, N, K;             // true sizes; K bounds the A loads
     int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
@@ -131,6 +135,17 @@ enum AMode { kAExact = 0, kABuf = 3, kAHalf = 4, kAXG = 5, kAXGS = 6, kAHalfBuf 
 // kEpiStoreHalf with the f16 output written in the perm32 k order, as the A
 // operand of a later kBSign product.
 constexpr int kEpiHalfScaleP = 7, kEpiStoreHalfP = 8;
+
+// Backward epilogues of the binary low-rank layer (v is the accumulated product,
+// f the factor rowf[n], E the operand ea; columns n >= nrowf are padding: their
+// f16 output is 0 and they have no partial sum).  Each keeps, per block of 32
+// output rows, the column sum of E*w over the block's rows (w as below; each
+// product rounded, then added in a fixed order) in part[row block][n]:
+//   kEpiBwdC:  w = v (the c of the forward); Ch[m][perm4(n)] = f16((E*f)*gs);
+//   kEpiBwdDb: w = v*alpha;                  Ch[m][perm32(n)] = f16((w*f)*gs);
+//   kEpiBwdDx: w = v*alpha;                  C[m][n] = f*w;
+//   kEpiBwdDxAcc: as kEpiBwdDx, C[m][n] = f32(C[m][n] + f32(f*w)).
+constexpr int kEpiBwdC = 9, kEpiBwdDb = 10, kEpiBwdDx = 11, kEpiBwdDxAcc = 12;
 
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool SCALED,
           int EPI, int ASTG, int KSUB, int BMODE>
@@ -565,6 +580,50 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     }
 
     // ---- epilogue: lane holds column lrow, rows 8*(r/4) + 4*hk + r%4 of each block
+    constexpr bool BWD = EPI == kEpiBwdC || EPI == kEpiBwdDb || EPI == kEpiBwdDx || EPI == kEpiBwdDxAcc;
+    if constexpr (BWD) {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                if (SPLIT && ((mb * NB + nb) < HALF) != (wk == 0)) continue;  // the partner group stores it (wave-uniform)
+                const int gn = n0 + wn * WTN + nb * 32 + lrow;
+                const int mblk = m0 + wm * WTM + mb * 32;  // first row of this 32-row block
+                const bool col = gn < p.N, real = gn < p.nrowf;
+                const float f = real ? p.rowf[gn] : 0.0f;
+                float psum = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = mblk + 8 * (r >> 2) + 4 * hk + (r & 3);
+                    if (gm < p.M && col) {
+                        const float v = acc[mb][nb][r];
+                        const int64_t row = (int64_t)gm;
+                        if constexpr (EPI == kEpiBwdC) {
+                            const float e = real ? p.ea[row * p.ldea + gn] : 0.0f;
+                            psum = psum + e * v;
+                            p.Ch[row * p.ldch + perm4(gn)] = (_Float16)((e * f) * p.gs);
+                        } else if constexpr (EPI == kEpiBwdDb) {
+                            const float w = v * p.alpha;
+                            const float e = real ? p.ea[row * p.ldea + gn] : 0.0f;
+                            psum = psum + e * w;
+                            p.Ch[row * p.ldch + perm32(gn)] = (_Float16)((w * f) * p.gs);
+                        } else {
+                            const float w = v * p.alpha;
+                            psum = psum + p.ea[row * p.ldea + gn] * w;
+                            float *c = p.C + row * p.ldc + gn;
+                            if constexpr (EPI == kEpiBwdDx) *c = f * w;
+                            else *c = *c + f * w;
+                        }
+                    }
+                }
+                // the block's other 16 rows are in lane ^ 32: both lanes form the
+                // same sum (addition is commutative), the lower one stores it
+                const float other = __shfl_xor(psum, 32);
+                if (hk == 0 && real && mblk < p.M) p.part[(int64_t)(mblk >> 5) * p.nrowf + gn] = psum + other;
+            }
+        return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll

@@ -186,13 +186,13 @@ int blr_forward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits
  * The two new products stage their inputs in f16 as f16(dy.h.gscale) and
  * f16(db.l.gscale) and multiply their f32 results by 1/gscale; gscale must be a
  * power of two in (0, 65536].  a and c are recomputed with the forward's kernels.
- * Sums over tokens are f32 in a fixed order (chunks of 16 tokens, then the chunks
- * in order), so results are reproducible.  dh [P][d_out], dl [P][r], dg [P][d_in]
+ * Sums over tokens are f32 in a fixed order (within each block of 32 tokens in
+ * a fixed order, then the blocks in order), so results are reproducible.  dh [P][d_out], dl [P][r], dg [P][d_in]
  * are accumulated (y = f32(y + s)); dx [M][d_in] is overwritten by path 0 and the
  * later paths add f32(g.dx') to it.  Operands as for blr_forward_paths, plus dy:
  * device f32 [M][d_out]; all device pointers 4-byte aligned and l 16-byte
  * aligned; outputs must not overlap each other or the inputs.
- * 1 <= P <= 4096; M <= 1048560 (65535 chunks of 16 tokens); M == 0 is a no-op.
+ * 1 <= P <= 4096; M == 0 is a no-op.
  * The workspace is the library's (as for blr_forward).
  * Preconditions (not checked): the forward's, and |dy.h.gscale| and |db.l.gscale|
  * within f16 range (choose gscale so that they are neither huge nor subnormal).
