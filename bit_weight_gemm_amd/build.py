@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq2.so")
-SOURCES = ["libtq2.cpp", "tq2_gemv.hip", "mfma_gemm.hip", "blr.hip", "skinny_gemm.hip"]
+SOURCES = ["libtq2.cpp", "repack.cpp", "tq2_gemv.hip", "mfma_gemm.hip", "blr.hip", "skinny_gemm.hip"]
 ARCH = "gfx950"
 
 

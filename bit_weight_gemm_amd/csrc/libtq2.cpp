@@ -13,6 +13,7 @@
 
 #include "../../include/libtq2.h"
 #include "internal.h"
+#include "repack.h"
 
 using tq2::DevWeight;
 
@@ -29,8 +30,6 @@ struct tq2_weight {
 };
 
 namespace {
-
-constexpr size_t kBlockBytes = 34;
 
 // gfx950 check, cached per device ordinal.
 int check_device(int *dev_out) {
@@ -86,16 +85,6 @@ int forced_path() {
     if (s && std::strcmp(s, "mfma") == 0) v = TQ2_PATH_MFMA;
     g_forced.store(v);
     return v;
-}
-
-// Pair-interleaved group word: element e of the 16 at bits 2*(e>>1) + 16*(e&1).
-inline uint32_t group_word(const uint8_t *qs4) {
-    uint32_t out = 0;
-    for (int e = 0; e < 16; ++e) {
-        const uint32_t code = (qs4[e >> 2] >> (2 * (e & 3))) & 3u;
-        out |= code << (2 * (e >> 1) + 16 * (e & 1));
-    }
-    return out;
 }
 
 
@@ -208,47 +197,22 @@ int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *strea
     const int64_t kb = K / tq2::kBlock;
     // kernels index rows with 32-bit integers: the padded row count must fit
     if (N > ((int64_t)1 << 31) - tq2::kRowPad || K > (int64_t)1 << 30) return TQ2_EINVAL;
-    if (nbytes != (size_t)N * (size_t)kb * kBlockBytes) return TQ2_EINVAL;
+    if (nbytes != (size_t)N * (size_t)kb * tq2::kBlockBytes) return TQ2_EINVAL;
     *out = nullptr;
     int dev = -1;
     int st = check_device(&dev);
     if (st) return st;
 
-    const uint8_t *src = static_cast<const uint8_t *>(aos);
-    const int64_t npad = (N + tq2::kRowPad - 1) / tq2::kRowPad * tq2::kRowPad;
-    const int64_t kw = K / 16;
-    const size_t codes_bytes = (size_t)npad * kw * 4;
-    const size_t scale_bytes = (size_t)npad * kb * 2;
-    const size_t scale_off = (codes_bytes + 255) / 256 * 256;
-    const size_t total = scale_off + (scale_bytes + 255) / 256 * 256;
-
+    const tq2::RepackLayout L = tq2::repack_layout(N, K);
+    const size_t total = L.total;
     bool mfma_ok = true;
     std::vector<uint8_t> host;
     try {
-        host.assign(total, 0);
+        host.resize(total);
     } catch (const std::bad_alloc &) {
         return TQ2_ENOMEM;
     }
-    uint32_t *hc = reinterpret_cast<uint32_t *>(host.data());
-    uint16_t *hs = reinterpret_cast<uint16_t *>(host.data() + scale_off);
-    for (int64_t n = 0; n < N; ++n) {
-        for (int64_t b = 0; b < kb; ++b) {
-            const uint8_t *blk = src + ((size_t)n * kb + b) * kBlockBytes;
-            const uint16_t d = (uint16_t)(blk[32] | (blk[33] << 8));
-            if (((d >> 10) & 31) == 31) return TQ2_EINVAL;  // NaN or infinite scale
-            bool has3 = false;
-            for (int g = 0; g < 8; ++g) {
-                const uint32_t wv = group_word(blk + 4 * g);
-                has3 |= ((wv & (wv >> 1)) & 0x55555555u) != 0;
-                hc[tq2::code_index(n, b * 8 + g, kw)] = wv;
-            }
-            // |2d| must stay within f16 for the MFMA operand (code 3 = +2d).
-            if (has3 && (d & 0x7fff) > 0x77ff) mfma_ok = false;
-            hs[tq2::scale_index(n, b, kb)] = d;
-        }
-    }
-    for (int64_t n = N; n < npad; ++n)
-        for (int64_t g = 0; g < kw; ++g) hc[tq2::code_index(n, g, kw)] = 0x55555555u;  // code 1 = weight 0
+    if (!tq2::repack_blocks(static_cast<const uint8_t *>(aos), L, host.data(), &mfma_ok)) return TQ2_EINVAL;
 
     tq2_weight *w = new (std::nothrow) tq2_weight;
     if (!w) return TQ2_ENOMEM;
@@ -269,9 +233,9 @@ int tq2_upload(const void *aos, size_t nbytes, int64_t N, int64_t K, void *strea
     w->device = dev;
     w->dev.N = N;
     w->dev.K = K;
-    w->dev.Npad = npad;
+    w->dev.Npad = L.npad;
     w->dev.codes = static_cast<uint32_t *>(dmem);
-    w->dev.scales = reinterpret_cast<uint16_t *>(static_cast<char *>(dmem) + scale_off);
+    w->dev.scales = reinterpret_cast<uint16_t *>(static_cast<char *>(dmem) + L.scale_off);
     w->dev.bytes = total;
     w->dev.mfma_ok = mfma_ok;
     *out = w;
