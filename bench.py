@@ -317,6 +317,29 @@ def bench_blr_backward(torch, bw, steps, warmup):
     return t
 
 
+def bench_blr_saved(torch, bw, steps, warmup):
+    """The layer forward that keeps a and c (blr_forward_paths_save) and the backward
+    from them (blr_backward_paths_saved), one path, timed separately."""
+    d = wl.blr_inputs()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    m, d_in = d["x"].shape
+    d_out, r = d["h"].size, d["l"].size
+    bu, bv = dev(d["bits_u"].view(np.int32)[None]), dev(d["bits_v"].view(np.int32)[None])
+    h, l, g, x = dev(d["h"][None]), dev(d["l"][None]), dev(d["g"][None]), dev(d["x"])
+    dy = dev((np.random.default_rng(4).standard_normal((m, d_out)) * 1e-3).astype(np.float32))
+    y = torch.empty((m, d_out), device="cuda")
+    saved = torch.empty(bw.blr_saved_size(1, m, d_in, d_out, r), dtype=torch.uint8, device="cuda")
+    tf = Timer(torch).run(lambda i: bw.blr_forward_paths_save(bu, bv, h, l, g, x, y, saved), steps, warmup)
+    dh, dl, dg = (torch.zeros((1, n), device="cuda") for n in (d_out, r, d_in))
+    dx = torch.empty((m, d_in), device="cuda")
+    tb = Timer(torch).run(lambda i: bw.blr_backward_paths_saved(bu, bv, h, l, g, x, dy, dh, dl, dg, saved, dx=dx),
+                          steps, warmup)
+    flop = 2.0 * m * r * (d_in + d_out)
+    return {"forward_save_ms": tf["step_ms"], "forward_save_ms_min": tf["step_ms_min"],
+            "backward_saved_ms": tb["step_ms"], "backward_saved_ms_min": tb["step_ms_min"],
+            "backward_saved_tflops_algorithmic": flop / (tb["step_ms"] * 1e-3) / 1e12}
+
+
 def calib_copy(torch, reps=5):
     """Untimed device copies of known size, for scaling the HBM byte counters."""
     a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -552,6 +575,8 @@ def main():
         log(f"[blr] {json.dumps(out['blr'])}")
         out["blr_backward"] = bench_blr_backward(torch, bw, max(K, 20), W)
         log(f"[blr backward] {json.dumps(out['blr_backward'])}")
+        out["blr_saved"] = bench_blr_saved(torch, bw, max(K, 20), W)
+        log(f"[blr saved] {json.dumps(out['blr_saved'])}")
 
     line = {
         "metric": "TQ2 GEMM weight-GB/s (M=1) and TFLOP/s (M=2048), % of HBM/MFMA roofline",
@@ -634,6 +659,14 @@ def main():
                                             "(a and c recomputed)",
                                 "tflops_algorithmic": round(b["tflops_step"], 2),
                                 "ms_per_call": b["step_ms"], "ms_per_call_min": b["step_ms_min"]}
+    if "blr_saved" in out:
+        b = out["blr_saved"]
+        line["blr_saved"] = {"workload": "blr_forward_paths_save, then blr_backward_paths_saved from the kept a and c "
+                                         "(one path, M=512, d_in=d_out=4096, r=1024)",
+                             "forward_save_ms": b["forward_save_ms"], "forward_save_ms_min": b["forward_save_ms_min"],
+                             "backward_saved_ms": b["backward_saved_ms"],
+                             "backward_saved_ms_min": b["backward_saved_ms_min"],
+                             "backward_saved_tflops_algorithmic": round(b["backward_saved_tflops_algorithmic"], 2)}
     if "cpu" in only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -8,7 +8,9 @@ raise.
 Names follow the C ABI in include/libtq2.h: tq2_upload, tq2_free, tq2_gemm,
 tq2_gemm_path, tq2_dequant, blr_forward, blr_forward_paths, blr_backward_paths
 (library-owned workspace), blr_forward_ws, blr_forward_paths_ws,
-blr_backward_paths_ws (caller-owned workspace), blr_workspace_size,
+blr_backward_paths_ws (caller-owned workspace), blr_forward_paths_save and
+blr_backward_paths_saved (activations kept by the forward for the backward),
+blr_saved_size, blr_workspace_size,
 blr_backward_workspace_size, tq2_workspace_allocs, tq2_select_path,
 tq2_set_path, tq2_set_m_small, tq2_strerror, tq2_version.
 
@@ -87,6 +89,10 @@ def lib():
         "blr_backward_paths_ws": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz,
                                    p], i32),
         "blr_backward_ws": ([p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz, p], i32),
+        "blr_saved_size": ([i64, i64, i64, i64, i64], sz),
+        "blr_forward_paths_save": ([i64, p, p, p, p, p, p, p, i64, i64, i64, i64, p, sz, p], i32),
+        "blr_backward_paths_saved": ([i64, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_float, p, sz,
+                                      p], i32),
         "tq2_strerror": ([i32], ctypes.c_char_p),
         "tq2_version": ([], ctypes.c_char_p),
     }
@@ -329,7 +335,61 @@ def blr_backward_workspace_size(m: int, d_in: int, d_out: int, r: int) -> int:
     return int(lib().blr_backward_workspace_size(m, d_in, d_out, r))
 
 
-def _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, workspace, use_ws):
+def blr_saved_size(paths: int, m: int, d_in: int, d_out: int, r: int) -> int:
+    return int(lib().blr_saved_size(int(paths), int(m), int(d_in), int(d_out), int(r)))
+
+
+def blr_forward_paths_save(bits_u, bits_v, h, l, g, x, y=None, saved=None, stream=None):
+    """blr_forward_paths that also keeps each path's a and c (f32) in `saved` (uint8,
+    >= blr_saved_size bytes; allocated if None) for blr_backward_paths_saved.
+    Returns (y, saved)."""
+    import torch
+
+    npaths, m, d_in, d_out, r = _blr_sizes(bits_u, bits_v, h, l, g, x, paths=True)
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
+    _shape(y, (m, d_out), "y")
+    need = blr_saved_size(npaths, m, d_in, d_out, r)
+    if need == 0:
+        raise Tq2Error(TQ2_EINVAL, "blr_saved_size")
+    if saved is None:
+        saved = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if saved.dim() != 1 or saved.numel() < need:
+        raise ValueError(f"saved must be a flat uint8 tensor of at least {need} bytes")
+    _check(lib().blr_forward_paths_save(
+        npaths, _dev(bits_u, torch.int32, "bits_u"), _dev(bits_v, torch.int32, "bits_v"),
+        _dev(h, torch.float32, "h"), _dev(l, torch.float32, "l"), _dev(g, torch.float32, "g"),
+        _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m, d_in, d_out, r,
+        _dev(saved, torch.uint8, "saved"), saved.numel(), _stream(stream)), "blr_forward_paths_save")
+    return y, saved
+
+
+def blr_saved_views(saved, paths: int, m: int, d_out: int, r: int):
+    """Per-path views (a [M][r], c [M][d_out]) of a buffer filled by blr_forward_paths_save."""
+    import torch
+
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    a_bytes = up(m * r * 4)
+    path_bytes = a_bytes + up(m * d_out * 4)
+    out = []
+    for q in range(paths):
+        base = q * path_bytes
+        a = saved[base: base + m * r * 4].view(torch.float32).view(m, r)
+        c = saved[base + a_bytes: base + a_bytes + m * d_out * 4].view(torch.float32).view(m, d_out)
+        out.append((a, c))
+    return out
+
+
+def blr_backward_paths_saved(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, saved, dx=None, gscale=1024.0,
+                             stream=None):
+    """blr_backward_paths from the activations blr_forward_paths_save kept in `saved`
+    (same layer and x): no recomputation, the same bits."""
+    return _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, None, False,
+                              saved=saved)
+
+
+def _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, stream, workspace, use_ws,
+                       saved=None):
     import torch
 
     npaths, m, d_in, d_out, r = _blr_sizes(bits_u, bits_v, h, l, g, x, paths=True)
@@ -346,7 +406,13 @@ def _blr_backward_call(bits_u, bits_v, h, l, g, x, dy, dh, dl, dg, dx, gscale, s
             _dev(dh, torch.float32, "dh"), _dev(dl, torch.float32, "dl"), _dev(dg, torch.float32, "dg"),
             m, d_in, d_out, r, float(gscale)]
     L = lib()
-    if use_ws:
+    if saved is not None:
+        need = blr_saved_size(npaths, m, d_in, d_out, r)
+        if saved.dim() != 1 or saved.numel() < need:
+            raise ValueError(f"saved must be a flat uint8 tensor of at least {need} bytes")
+        _check(L.blr_backward_paths_saved(*args, _dev(saved, torch.uint8, "saved"), saved.numel(),
+                                          _stream(stream)), "blr_backward_paths_saved")
+    elif use_ws:
         ws = _workspace(workspace, blr_backward_workspace_size(m, d_in, d_out, r), x, stream,
                         "blr_backward_workspace_size")
         _check(L.blr_backward_paths_ws(*args, _dev(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)),

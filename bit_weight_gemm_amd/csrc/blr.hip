@@ -105,16 +105,30 @@ static GemmArgs gemm2_args(const BlrPlan &pl, const uint32_t *bits_u, const _Flo
 
 hipError_t launch_blr_forward(const BlrPlan &pl, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
-                              void *workspace, bool accumulate, hipStream_t s) {
+                              void *workspace, bool accumulate, float *save_a, float *save_c, hipStream_t s) {
     _Float16 *al = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + pl.off_al);
+    const bool save = save_a != nullptr;
     // GEMM1: al[M][kpad2] = f16(l . (f16(x.g) . S_V)), 0 in the columns past r
+    // (saving: also a[M][r] in f32, as the backward's recomputation writes it)
     GemmArgs p1 = gemm1_args(pl, bits_v, g, x);
-    p1.Ch = al, p1.ldc = pl.kpad2, p1.rowf = l, p1.nrowf = (int)pl.r;
-    hipError_t e = run_gemm1<kEpiHalfScaleP>(p1, pl, xg_vector(pl, x, g), s);
+    p1.rowf = l, p1.nrowf = (int)pl.r;
+    hipError_t e;
+    if (save) {
+        p1.C = save_a, p1.ldc = pl.r, p1.Ch = al, p1.ldch = pl.kpad2;
+        e = run_gemm1<kEpiStoreHalfP>(p1, pl, xg_vector(pl, x, g), s);
+    } else {
+        p1.Ch = al, p1.ldc = pl.kpad2;
+        e = run_gemm1<kEpiHalfScaleP>(p1, pl, xg_vector(pl, x, g), s);
+    }
     if (e != hipSuccess) return e;
-    // GEMM2: y = h . (al . S_U^T) (later paths of a layer: y = f32(y + f32(h . c)))
+    // GEMM2: y = h . (al . S_U^T) (later paths of a layer: y = f32(y + f32(h . c)));
+    // saving: also c[M][d_out] itself
     GemmArgs p2 = gemm2_args(pl, bits_u, al);
     p2.C = y, p2.ldc = pl.d_out, p2.rowf = h;
+    if (save) {
+        p2.Cs = save_c, p2.ldcs = pl.d_out;
+        return accumulate ? gemm_short_k<kEpiRowScaleAccSave>(p2, s) : gemm_short_k<kEpiRowScaleSave>(p2, s);
+    }
     return accumulate ? gemm_short_k<kEpiRowScaleAcc>(p2, s) : gemm_short_k<kEpiRowScale>(p2, s);
 }
 
@@ -166,6 +180,58 @@ BlrBwdPlan blr_bwd_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 
 namespace {
 
+// With the forward's c saved: for each block of 32 tokens and column n < N
+// (d_out padded), the partial sum of dy.c over the block's tokens, in the order
+// c's epilogue (kEpiBwdC) adds them (tokens 8i+j, then 8i+4+j, for i, j = 0..3,
+// each half summed in that order and the halves added), so the same bits; and
+// dyh[t][perm4(n)] = f16((dy*h)*gs), 0 for the padding columns n >= d_out.
+struct DycArgs {
+    const float *dy, *c, *h;   // dy, c [M][d_out]; h [d_out]
+    _Float16 *dyh;             // [M][ldh]
+    float *part;               // [blocks][d_out]
+    int64_t M, d_out, N, ldh, blocks;
+    float gs;
+};
+
+// One thread per column and block of 32 tokens; each half-block's 16 values of dy
+// and c are loaded before any is used, so the loads of a thread go out together.
+__global__ __launch_bounds__(256) void blr_dyc_kernel(DycArgs q) {
+#pragma clang fp contract(off)
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= q.N) return;
+    const float *__restrict__ dy = q.dy;
+    const float *__restrict__ c = q.c;
+    _Float16 *__restrict__ dyh = q.dyh;
+    const bool real = n < q.d_out;
+    const float f = real ? q.h[n] : 0.0f;
+    const int64_t hn = perm4((int)n);  // n < 2^30
+    for (int64_t b = blockIdx.y; b < q.blocks; b += gridDim.y) {
+        float half[2];
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+            float e[16], v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t t = 32 * b + 8 * (r >> 2) + 4 * hk + (r & 3);
+                const bool live = real && t < q.M;
+                e[r] = live ? dy[t * q.d_out + n] : 0.0f;
+                v[r] = live ? c[t * q.d_out + n] : 0.0f;
+            }
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t t = 32 * b + 8 * (r >> 2) + 4 * hk + (r & 3);
+                if (t < q.M) {
+                    if (real) psum = psum + e[r] * v[r];
+                    dyh[t * q.ldh + hn] = (_Float16)((e[r] * f) * q.gs);
+                }
+            }
+            half[hk] = psum;
+        }
+        if (real) q.part[b * q.d_out + n] = half[0] + half[1];
+    }
+}
+
 // out[n] = f32(out[n] + f32(sum over row blocks b in order of part[b][n])) for the
 // three gradients of a path (dh: d_out columns, dl: r, dg: d_in), one thread per
 // column; the loads of a group of blocks are independent, so they go out
@@ -203,37 +269,18 @@ __global__ __launch_bounds__(256) void blr_finish_kernel(FinishArgs q) {
 
 }  // namespace
 
-hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
-                               const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
-                               float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s) {
+// db, dx' and the finish of a path's backward, from dyh and a (launches 3 to 5).
+static hipError_t backward_tail(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v, const float *l,
+                                const float *g, const float *x, const float *a, float *dx, float *dh, float *dl,
+                                float *dg, float gs, char *ws, bool accumulate_dx, bool small, hipStream_t s) {
     const BlrPlan &pl = pb.fwd;
     const int64_t M = pl.M, d_in = pl.d_in, d_out = pl.d_out, r = pl.r;
-    char *ws = static_cast<char *>(workspace);
-    auto at = [&](size_t off) { return ws + off; };
-    _Float16 *al = reinterpret_cast<_Float16 *>(at(pl.off_al));
-    float *a = reinterpret_cast<float *>(at(pb.off_a));
-    _Float16 *dyh = reinterpret_cast<_Float16 *>(at(pb.off_dyh));
-    _Float16 *dbl = reinterpret_cast<_Float16 *>(at(pb.off_dbl));
-    float *part_dh = reinterpret_cast<float *>(at(pb.off_part_dh));
-    float *part_dl = reinterpret_cast<float *>(at(pb.off_part_dl));
-    float *part_dg = reinterpret_cast<float *>(at(pb.off_part_dg));
+    _Float16 *dyh = reinterpret_cast<_Float16 *>(ws + pb.off_dyh);
+    _Float16 *dbl = reinterpret_cast<_Float16 *>(ws + pb.off_dbl);
+    float *part_dh = reinterpret_cast<float *>(ws + pb.off_part_dh);
+    float *part_dl = reinterpret_cast<float *>(ws + pb.off_part_dl);
+    float *part_dg = reinterpret_cast<float *>(ws + pb.off_part_dg);
     hipError_t e;
-    const bool small = blr_small_tiles(M, pl.kpad2);
-    // a = f16(x.g) . S_V [M][r] in f32, and al = f16(l.a) [M][kpad2] as the forward's GEMM1 writes it
-    {
-        GemmArgs p = gemm1_args(pl, bits_v, g, x);
-        p.C = a, p.ldc = r, p.Ch = al, p.ldch = pl.kpad2, p.rowf = l, p.nrowf = (int)r;
-        e = run_gemm1<kEpiStoreHalfP>(p, pl, xg_vector(pl, x, g), s);
-        if (e != hipSuccess) return e;
-    }
-    // c = al . S_U^T (not stored): partial sums of dy.c, and dyh = f16(dy.h.gs) [M][kpado] (perm4 order)
-    {
-        GemmArgs p = gemm2_args(pl, bits_u, al);
-        p.N = (int)pb.kpado, p.nrowf = (int)d_out, p.rowf = h;
-        p.ea = dy, p.ldea = d_out, p.part = part_dh, p.Ch = dyh, p.ldch = pb.kpado, p.gs = gs;
-        e = gemm_short_k<kEpiBwdC>(p, s);
-        if (e != hipSuccess) return e;
-    }
     // db = dyh . S_U / gs (not stored; contraction over d_out, down the rows of bits_u):
     // partial sums of a.db, and dbl = f16(db.l.gs) [M][kpad2] (perm32 order)
     {
@@ -260,18 +307,66 @@ hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, con
         if (e != hipSuccess) return e;
     }
     // dh, dl, dg += their partial sums, the row blocks in order
+    FinishArgs q{};
+    q.job[0] = FinishJob{part_dh, dh, d_out};
+    q.job[1] = FinishJob{part_dl, dl, r};
+    q.job[2] = FinishJob{part_dg, dg, d_in};
+    q.blocks = pb.blocks;
+    const int64_t cols = d_out + r + d_in;
+    blr_finish_kernel<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s>>>(q);
+    return hipGetLastError();
+}
+
+hipError_t launch_blr_backward(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                               const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                               float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s) {
+    const BlrPlan &pl = pb.fwd;
+    const int64_t M = pl.M, d_out = pl.d_out, r = pl.r;
+    char *ws = static_cast<char *>(workspace);
+    _Float16 *al = reinterpret_cast<_Float16 *>(ws + pl.off_al);
+    float *a = reinterpret_cast<float *>(ws + pb.off_a);
+    hipError_t e;
+    // a = f16(x.g) . S_V [M][r] in f32, and al = f16(l.a) [M][kpad2] as the forward's GEMM1 writes it
     {
-        FinishArgs q{};
-        q.job[0] = FinishJob{part_dh, dh, d_out};
-        q.job[1] = FinishJob{part_dl, dl, r};
-        q.job[2] = FinishJob{part_dg, dg, d_in};
-        q.blocks = pb.blocks;
-        const int64_t cols = d_out + r + d_in;
-        blr_finish_kernel<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s>>>(q);
-        e = hipGetLastError();
+        GemmArgs p = gemm1_args(pl, bits_v, g, x);
+        p.C = a, p.ldc = r, p.Ch = al, p.ldch = pl.kpad2, p.rowf = l, p.nrowf = (int)r;
+        e = run_gemm1<kEpiStoreHalfP>(p, pl, xg_vector(pl, x, g), s);
         if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+    // c = al . S_U^T (not stored): partial sums of dy.c, and dyh = f16(dy.h.gs) [M][kpado] (perm4 order)
+    {
+        GemmArgs p = gemm2_args(pl, bits_u, al);
+        p.N = (int)pb.kpado, p.nrowf = (int)d_out, p.rowf = h;
+        p.ea = dy, p.ldea = d_out, p.part = reinterpret_cast<float *>(ws + pb.off_part_dh);
+        p.Ch = reinterpret_cast<_Float16 *>(ws + pb.off_dyh), p.ldch = pb.kpado, p.gs = gs;
+        e = gemm_short_k<kEpiBwdC>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    return backward_tail(pb, bits_u, bits_v, l, g, x, a, dx, dh, dl, dg, gs, ws, accumulate_dx,
+                         blr_small_tiles(M, pl.kpad2), s);
+}
+
+// The backward from the forward's saved a [M][r] and c [M][d_out] (f32, as the
+// forward computed them): the dy.c sums and dyh in one pass over dy and c, then
+// the same db, dx' and finish launches, so four launches instead of five and no
+// recomputation; the bits are those of the recomputing backward.
+hipError_t launch_blr_backward_saved(const BlrBwdPlan &pb, const uint32_t *bits_u, const uint32_t *bits_v,
+                                     const float *h, const float *l, const float *g, const float *x, const float *dy,
+                                     const float *a, const float *c, float *dx, float *dh, float *dl, float *dg,
+                                     float gs, void *workspace, bool accumulate_dx, hipStream_t s) {
+    const BlrPlan &pl = pb.fwd;
+    char *ws = static_cast<char *>(workspace);
+    DycArgs q{};
+    q.dy = dy, q.c = c, q.h = h;
+    q.dyh = reinterpret_cast<_Float16 *>(ws + pb.off_dyh);
+    q.part = reinterpret_cast<float *>(ws + pb.off_part_dh);
+    q.M = pl.M, q.d_out = pl.d_out, q.N = pb.kpado, q.ldh = pb.kpado, q.blocks = pb.blocks, q.gs = gs;
+    const unsigned gy = (unsigned)(pb.blocks < 65535 ? pb.blocks : 65535);
+    blr_dyc_kernel<<<dim3((unsigned)((pb.kpado + 255) / 256), gy), dim3(256), 0, s>>>(q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return backward_tail(pb, bits_u, bits_v, l, g, x, a, dx, dh, dl, dg, gs, ws, accumulate_dx,
+                         blr_small_tiles(pl.M, pl.kpad2), s);
 }
 
 }  // namespace tq2

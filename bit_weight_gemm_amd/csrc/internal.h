@@ -52,9 +52,15 @@ hipError_t launch_blr_backward(const BlrBwdPlan &p, const uint32_t *bits_u, cons
                                const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
                                float *dl, float *dg, float gs, void *workspace, bool accumulate_dx, hipStream_t s);
 
-// accumulate: y = f32(y + f32(h*c)) instead of y = f32(h*c) (later paths of a layer)
+// accumulate: y = f32(y + f32(h*c)) instead of y = f32(h*c) (later paths of a layer);
+// save_a / save_c (both or neither): also keep a [M][r] and c [M][d_out] in f32
 hipError_t launch_blr_forward(const BlrPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,
                               const float *h, const float *l, const float *g, const float *x, float *y,
-                              void *workspace, bool accumulate, hipStream_t s);
+                              void *workspace, bool accumulate, float *save_a, float *save_c, hipStream_t s);
+// the backward from a forward's saved a and c (no recomputation; the same bits)
+hipError_t launch_blr_backward_saved(const BlrBwdPlan &p, const uint32_t *bits_u, const uint32_t *bits_v,
+                                     const float *h, const float *l, const float *g, const float *x, const float *dy,
+                                     const float *a, const float *c, float *dx, float *dh, float *dl, float *dg,
+                                     float gs, void *workspace, bool accumulate_dx, hipStream_t s);
 
 }  // namespace tq2

@@ -8,6 +8,8 @@
 #include <cstring>
 #include <memory>
 #include <mutex>
+#include <initializer_list>
+#include <utility>
 #include <new>
 #include <vector>
 
@@ -358,15 +360,34 @@ int workspace_check(const void *ws, size_t ws_bytes, size_t need, const void *ou
     return TQ2_OK;
 }
 
-// The paths one after another, sharing one path's workspace (checked arguments).
+// Saved activations of a layer's forward (blr_forward_paths_save): per path, a
+// [M][r] then c [M][d_out], f32, each 256-byte aligned.
+struct SavedLayout {
+    size_t a_bytes, c_off, path_bytes;
+};
+SavedLayout saved_layout(int64_t M, int64_t d_out, int64_t r) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    SavedLayout L{};
+    L.a_bytes = up((size_t)M * r * 4);
+    L.c_off = L.a_bytes;
+    L.path_bytes = L.c_off + up((size_t)M * d_out * 4);
+    return L;
+}
+
+// The paths one after another, sharing one path's workspace (checked arguments);
+// with `saved`, each path also keeps its a and c there.
 int blr_forward_launch(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                        const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out, int64_t r,
-                       void *workspace, hipStream_t s) {
+                       void *workspace, hipStream_t s, void *saved = nullptr) {
     const tq2::BlrPlan plan = tq2::blr_plan(M, d_in, d_out, r);
+    const SavedLayout sl = saved_layout(M, d_out, r);
     const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
     for (int64_t p = 0; p < P; ++p) {
+        char *sp = saved ? static_cast<char *>(saved) + (size_t)p * sl.path_bytes : nullptr;
+        float *sa = sp ? reinterpret_cast<float *>(sp) : nullptr;
+        float *sc = sp ? reinterpret_cast<float *>(sp + sl.c_off) : nullptr;
         const int st = from_hip(tq2::launch_blr_forward(plan, bits_u + p * wu, bits_v + p * wv, h + p * d_out,
-                                                        l + p * r, g + p * d_in, x, y, workspace, p > 0, s));
+                                                        l + p * r, g + p * d_in, x, y, workspace, p > 0, sa, sc, s));
         if (st) return st;
     }
     return TQ2_OK;
@@ -419,15 +440,37 @@ int backward_workspace_check(const void *ws, size_t ws_bytes, size_t need, int64
 int blr_backward_launch(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
                         const float *g, const float *x, const float *dy, float *dx, float *dh, float *dl, float *dg,
                         int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace,
-                        hipStream_t s) {
+                        hipStream_t s, const void *saved = nullptr) {
     const tq2::BlrBwdPlan plan = tq2::blr_bwd_plan(M, d_in, d_out, r);
+    const SavedLayout sl = saved_layout(M, d_out, r);
     const int64_t wu = d_out * (r / 32), wv = d_in * (r / 32);
     for (int64_t q = 0; q < P; ++q) {
-        const int st = from_hip(tq2::launch_blr_backward(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out,
-                                                         l + q * r, g + q * d_in, x, dy, dx, dh + q * d_out,
-                                                         dl + q * r, dg + q * d_in, gscale, workspace, q > 0, s));
+        hipError_t e;
+        if (saved) {
+            const char *sp = static_cast<const char *>(saved) + (size_t)q * sl.path_bytes;
+            e = tq2::launch_blr_backward_saved(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out, l + q * r,
+                                               g + q * d_in, x, dy, reinterpret_cast<const float *>(sp),
+                                               reinterpret_cast<const float *>(sp + sl.c_off), dx, dh + q * d_out,
+                                               dl + q * r, dg + q * d_in, gscale, workspace, q > 0, s);
+        } else {
+            e = tq2::launch_blr_backward(plan, bits_u + q * wu, bits_v + q * wv, h + q * d_out, l + q * r,
+                                         g + q * d_in, x, dy, dx, dh + q * d_out, dl + q * r, dg + q * d_in, gscale,
+                                         workspace, q > 0, s);
+        }
+        const int st = from_hip(e);
         if (st) return st;
     }
+    return TQ2_OK;
+}
+
+// The caller's buffer of saved activations: large enough for P paths, 256-byte
+// aligned, clear of the buffers listed (which it must not overlap).
+int saved_check(const void *saved, size_t saved_bytes, int64_t P, int64_t M, int64_t d_out, int64_t r,
+                std::initializer_list<std::pair<const void *, size_t>> others) {
+    const size_t need = (size_t)P * saved_layout(M, d_out, r).path_bytes;
+    if (!saved || saved_bytes < need || (reinterpret_cast<uintptr_t>(saved) & 255u)) return TQ2_EINVAL;
+    for (const auto &o : others)
+        if (overlap(saved, need, o.first, o.second)) return TQ2_EINVAL;
     return TQ2_OK;
 }
 
@@ -494,6 +537,55 @@ int blr_forward_noalloc(const uint32_t *bits_u, const uint32_t *bits_v, const fl
     // every byte of the workspace that the launches read, they first write: no clearing needed
     return blr_forward_launch(1, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, ws,
                               static_cast<hipStream_t>(stream));
+}
+
+size_t blr_saved_size(int64_t P, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    if (P < 1 || P > 4096 || blr_workspace_size(M, d_in, d_out, r) == 0) return 0;
+    const size_t total = (size_t)P * saved_layout(M, d_out, r).path_bytes;
+    return total > 256 ? total : 256;  // 0 means bad sizes
+}
+
+int blr_forward_paths_save(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                           const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
+                           int64_t r, void *saved, size_t saved_bytes, void *stream) {
+    int st = blr_forward_check(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    const size_t p = (size_t)P;
+    st = saved_check(saved, saved_bytes, P, M, d_out, r,
+                     {{y, (size_t)M * d_out * 4}, {x, (size_t)M * d_in * 4}, {bits_u, p * d_out * (r / 32) * 4},
+                      {bits_v, p * d_in * (r / 32) * 4}, {h, p * d_out * 4}, {l, p * r * 4}, {g, p * d_in * 4}});
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Pool &pool = pool_for(dev, s);
+    std::lock_guard<std::mutex> lock(pool.mu);
+    st = pool_reserve(pool, blr_workspace_size(M, d_in, d_out, r));
+    if (st) return st;
+    return blr_forward_launch(P, bits_u, bits_v, h, l, g, x, y, M, d_in, d_out, r, pool.ptr, s, saved);
+}
+
+int blr_backward_paths_saved(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                             const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                             float *dl, float *dg, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale,
+                             const void *saved, size_t saved_bytes, void *stream) {
+    int st = blr_backward_check(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale);
+    if (st) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st || M == 0) return st;
+    const size_t p = (size_t)P;
+    st = saved_check(saved, saved_bytes, P, M, d_out, r,
+                     {{dx, (size_t)M * d_in * 4}, {dh, p * d_out * 4}, {dl, p * r * 4}, {dg, p * d_in * 4}});
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Pool &pool = pool_for(dev, s);
+    std::lock_guard<std::mutex> lock(pool.mu);
+    st = pool_reserve(pool, blr_backward_workspace_size(M, d_in, d_out, r));
+    if (st) return st;
+    return blr_backward_launch(P, bits_u, bits_v, h, l, g, x, dy, dx, dh, dl, dg, M, d_in, d_out, r, gscale, pool.ptr,
+                               s, saved);
 }
 
 int blr_backward_paths_ws(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,

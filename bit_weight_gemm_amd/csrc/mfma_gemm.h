@@ -84,6 +84,8 @@ struct GemmArgs {
     int64_t ldea;
     float *part;             // backward epilogues: column partial sums [ceil(M/32)][nrowf]
     float gs;                // backward epilogues: gradient scale of the f16 output
+    float *Cs;               // kEpiRowScaleSave / kEpiRowScaleAccSave: the product itself, [M][ldcs]
+    int64_t ldcs;
     int M, N, K;             // true sizes; K bounds the A loads
     int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
@@ -146,6 +148,10 @@ constexpr int kEpiHalfScaleP = 7, kEpiStoreHalfP = 8;
 //   kEpiBwdDx: w = v*alpha;                  C[m][n] = f*w;
 //   kEpiBwdDxAcc: as kEpiBwdDx, C[m][n] = f32(C[m][n] + f32(f*w)).
 constexpr int kEpiBwdC = 9, kEpiBwdDb = 10, kEpiBwdDx = 11, kEpiBwdDxAcc = 12;
+
+// kEpiRowScale and kEpiRowScaleAcc that also keep the product v itself in
+// Cs[m][n] (the binary low-rank forward's c, saved for the backward).
+constexpr int kEpiRowScaleSave = 13, kEpiRowScaleAccSave = 14;
 
 template <int BM, int BN, int WM, int WN, int WK, int STAGES, int BDEPTH, int AMODE, bool SCALED,
           int EPI, int ASTG, int KSUB, int BMODE>
@@ -632,7 +638,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
             if (gn >= p.N) continue;
             float rf = 1.0f;
-            if constexpr (EPI == kEpiRowScale || EPI == kEpiRowScaleAcc) rf = p.rowf[gn];
+            constexpr bool SAVE = EPI == kEpiRowScaleSave || EPI == kEpiRowScaleAccSave;
+            constexpr bool ACC = EPI == kEpiRowScaleAcc || EPI == kEpiRowScaleAccSave;
+            if constexpr (EPI == kEpiRowScale || ACC || SAVE) rf = p.rowf[gn];
             constexpr bool HALF_OUT = EPI == kEpiHalfScale || EPI == kEpiStoreHalf || EPI == kEpiHalfScaleP ||
                                       EPI == kEpiStoreHalfP;
             constexpr bool PERM_OUT = EPI == kEpiHalfScaleP || EPI == kEpiStoreHalfP;
@@ -650,7 +658,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                     } else if constexpr (EPI == kEpiStoreHalf || EPI == kEpiStoreHalfP) {
                         if (gn < p.nrowf) C[(int64_t)gm * p.ldc + gn] = v;
                         p.Ch[(int64_t)gm * p.ldch + hn] = (_Float16)(rf * v);
-                    } else if constexpr (EPI == kEpiRowScaleAcc) {
+                    } else if constexpr (ACC) {
                         // two roundings: the product must not be fused into the sum
 #pragma clang fp contract(off)
                         float *c = C + (int64_t)gm * p.ldc + gn;
@@ -659,7 +667,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                     } else if constexpr (EPI == kEpiStoreNT) {
                         __builtin_nontemporal_store(v, &C[(int64_t)gm * p.ldc + gn]);
                     } else
-                        C[(int64_t)gm * p.ldc + gn] = (EPI == kEpiRowScale || EPI == kEpiScale) ? rf * v : v;
+                        C[(int64_t)gm * p.ldc + gn] =
+                            (EPI == kEpiRowScale || EPI == kEpiRowScaleSave || EPI == kEpiScale) ? rf * v : v;
+                    if constexpr (SAVE) p.Cs[(int64_t)gm * p.ldcs + gn] = v;
                 }
             }
         }

@@ -221,6 +221,35 @@ int blr_backward_ws(const uint32_t *bits_u, const uint32_t *bits_v, const float 
                     int64_t d_in, int64_t d_out, int64_t r, float gscale, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* Bytes of the buffer that keeps a layer's activations for its backward: per
+ * path, a [M][r] then c [M][d_out], f32, each part 256-byte aligned (0 on bad
+ * sizes). */
+size_t blr_saved_size(int64_t P, int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/* [BLR] blr_forward_paths that also keeps, per path, a = (x.g) S_V and
+ * c = (a.l) S_U^T (the f32 values the forward computed) in `saved`, as the
+ * page's blr_forward keeps a and c in its scratch for blr_backward.  y has the
+ * bits blr_forward_paths gives.  saved: caller-owned device memory of at least
+ * blr_saved_size(P, M, d_in, d_out, r) bytes, 256-byte aligned, overlapping
+ * neither y nor the inputs; its previous contents are overwritten.  Otherwise as
+ * blr_forward_paths (library-owned workspace).  Asynchronous on `stream`. */
+int blr_forward_paths_save(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                           const float *g, const float *x, float *y, int64_t M, int64_t d_in, int64_t d_out,
+                           int64_t r, void *saved, size_t saved_bytes, void *stream);
+
+/* [BLR] blr_backward_paths from the activations a blr_forward_paths_save call
+ * kept in `saved` (same P, M, d_in, d_out, r, bitmaps, h, l, g and x; this is
+ * not checked): the page's blr_backward, which reads a and c from the forward
+ * instead of recomputing them.  Per path, one pass over dy and c forms the sums
+ * of dy.c and f16(dy.h.gscale), then db, dx' and the sums as in
+ * blr_backward_paths: four launches per path instead of five, and the same bits
+ * as blr_backward_paths.  saved must not overlap the outputs; everything else
+ * as for blr_backward_paths.  Asynchronous on `stream`. */
+int blr_backward_paths_saved(int64_t P, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                             const float *l, const float *g, const float *x, const float *dy, float *dx, float *dh,
+                             float *dl, float *dg, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float gscale,
+                             const void *saved, size_t saved_bytes, void *stream);
+
 /* Number of device allocations the library has made for its own workspaces
  * since the process started (grow-only: a call that fits the buffer its
  * (device, stream) already holds allocates nothing).  The page's GEMM keeps a

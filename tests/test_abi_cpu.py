@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
                  "blr_forward_paths", "blr_backward", "blr_backward_paths", "blr_forward_ws", "blr_forward_paths_ws",
                  "blr_backward_ws", "blr_backward_paths_ws", "blr_workspace_size", "blr_backward_workspace_size",
                  "tq2_select_path", "tq2_set_path", "tq2_set_m_small", "tq2_workspace_allocs", "tq2_strerror",
-                 "tq2_version", "tq2_weight_info"):
+                 "tq2_version", "tq2_weight_info", "blr_saved_size", "blr_forward_paths_save",
+                 "blr_backward_paths_saved"):
         assert must in names, must
 
 
@@ -147,6 +148,28 @@ def test_blr_backward_rejects_bad_arguments_on_the_host(L):
                                 f(1.0), None) == bw.TQ2_EINVAL
     assert L.blr_backward_paths_ws(1, None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8, 32,
                                    f(1.0), None, 0, None) == bw.TQ2_EINVAL
+
+
+def test_saved_size_rules(L):
+    """a [M][r] then c [M][d_out] in f32 per path, each part 256-byte aligned."""
+    assert bw.blr_saved_size(1, 512, 4096, 4096, 1024) == 512 * 1024 * 4 + 512 * 4096 * 4
+    assert bw.blr_saved_size(2, 3, 40, 24, 64) == 2 * (768 + 512)   # a: 768 bytes; c: 288 -> 512 per path
+    assert bw.blr_saved_size(0, 3, 40, 24, 64) == 0      # no paths
+    assert bw.blr_saved_size(1, 3, 40, 24, 33) == 0      # r % 32 != 0
+    assert bw.blr_saved_size(1, 0, 40, 24, 32) > 0       # M == 0 is valid (no-op)
+
+
+def test_saved_entry_points_reject_bad_arguments_on_the_host(L):
+    f = ctypes.c_float
+    assert L.blr_forward_paths_save(1, None, None, None, None, None, None, None, 4, 8, 8, 33, None, 0,
+                                    None) == bw.TQ2_EINVAL
+    assert L.blr_forward_paths_save(0, None, None, None, None, None, None, None, 4, 8, 8, 32, None, 0,
+                                    None) == bw.TQ2_EINVAL
+    assert L.blr_backward_paths_saved(1, None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8,
+                                      32, f(3.0), None, 0, None) == bw.TQ2_EINVAL
+    assert L.blr_backward_paths_saved(1, None, None, None, None, None, None, None, None, None, None, None, 4, 8, 8,
+                                      32, f(1.0), None, 0, None) == bw.TQ2_EINVAL
+    assert bw.tq2_workspace_allocs() == 0
 
 
 def test_bench_refuses_more_than_one_gpu():
