@@ -106,11 +106,14 @@ __device__ __forceinline__ int lds_off(int row, int kc) {
     const int g = NCH == 8 ? (row & 7) ^ ((row >> 3) & 1) : (row & 15);
     return row * (NCH * 8) + ((kc ^ g) << 3);
 }
-// B tile: slot of row R's 16-byte unit (its four code words of a 64-wide k
-// slice).  The transposing store writes word g of rows 4q+r from lane 4q+g, the
-// fragment read takes the units of 16 consecutive rows; this permutation within
-// each group of 16 rows spreads both over all banks.
-__device__ __forceinline__ int b_slot(int row) { return row ^ ((row >> 2) & 15); }
+// B tile: slot of row R's 16-byte unit (its four code words of 64-wide k slice
+// sl of the step).  The transposing store writes, per instruction, word g%4 of
+// rows 4q+r for every slice and row quad a wave covers; the fragment read takes
+// the units of 16 consecutive rows of one slice.  The row permutation within
+// each group of 16 rows, XORed with 2*sl, puts both on distinct banks for every
+// tile shape used (without the slice term a step of eight slices, whose slices
+// lie a multiple of 1 KB apart, stored eight lanes to each bank).
+__device__ __forceinline__ int b_slot(int row, int sl) { return row ^ ((row >> 2) & 15) ^ ((2 * sl) & 15); }
 
 // AMODE: how A tiles are read.  kAExact: f32, K is a multiple of the step and
 // rows past M read row M-1 (ternary GEMM).  kABuf: as kAExact, but through a
@@ -382,7 +385,8 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 const int item = (tid + i * T) % BITEMS;
                 const int r0 = (item / (4 * NSL)) * 4, g = item % (4 * NSL);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Bsm[st][(g >> 2) * (BN * 4) + b_slot(r0 + r) * 4 + (g & 3)] = breg[sb][i][r];
+                for (int r = 0; r < 4; ++r)
+                    Bsm[st][(g >> 2) * (BN * 4) + b_slot(r0 + r, g >> 2) * 4 + (g & 3)] = breg[sb][i][r];
             }
             if (SCALED && (DITEMS % 64 != 0 || tid < DITEMS)) {
                 const int unit = tid % DITEMS, quad = unit % (BN / 4), blk = unit / (BN / 4);
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             for (int nb = 0; nb < NB; ++nb) {
                 const int row = wn * WTN + nb * 32 + lrow;
                 if constexpr (BMODE == kBCodes) {
-                    bw[nb] = *reinterpret_cast<const u4 *>(&Bsm[st][sl * (BN * 4) + b_slot(row) * 4]);
+                    bw[nb] = *reinterpret_cast<const u4 *>(&Bsm[st][sl * (BN * 4) + b_slot(row, sl) * 4]);
                     dv[nb] = SCALED ? Ds[st][(sl * BK) / kBlock][row] : (_Float16)1.0f;
                 } else if constexpr (BMODE == kBSign) {
                     sw2[nb] = *reinterpret_cast<const uint2 *>(&Bsm[st][row * SROW + 2 * sl]);
