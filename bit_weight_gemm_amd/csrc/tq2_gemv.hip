@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
 
-    for (int kp = 0; kp < K; kp += 4096) {
+    for (int kp = 0;;) {  // K >= 128: the first pass always runs (see gemv_mt_kernel)
         const int g = (kp >> 4) + wave * 64 + lane;  // group index within the row
         if (g < kw) {
             // Issue every load of this pass before any arithmetic, so the whole
@@ -139,6 +139,8 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const uint32_t *__restric
                 }
             }
         }
+        kp += 4096;
+        if (kp >= K) break;
     }
 
     const int k32 = kept32(), k16 = kept16();
@@ -196,7 +198,9 @@ __global__ __launch_bounds__(256 * Q) void gemv_mt_kernel(const uint32_t *__rest
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
-    for (int kp = 0; kp < K; kp += 4096) {
+    // K >= 128 (checked at upload): the first pass always runs, so the kernel
+    // reads all its arguments in one scalar load instead of testing K first
+    for (int kp = 0;;) {
         const int g = (kp >> 4) + kwave * 64 + lane;  // group index within the row
         if (g < kw) {
             // all loads of the pass before any arithmetic: one memory round trip; the
@@ -240,6 +244,8 @@ __global__ __launch_bounds__(256 * Q) void gemv_mt_kernel(const uint32_t *__rest
                 }
             }
         }
+        kp += 4096;
+        if (kp >= K) break;
     }
     // per activation row: rows r and r+2 pairwise across the lane halves, then
     // across 16-lane rows, then DPP within each 16-lane row: row k16 + 2*k32's
