@@ -193,43 +193,72 @@ struct DycArgs {
     float gs;
 };
 
-// One thread per column and block of 32 tokens; each half-block's 16 values of dy
-// and c are loaded before any is used, so the loads of a thread go out together.
-__global__ __launch_bounds__(256) void blr_dyc_kernel(DycArgs q) {
+// Thread (column group, half, block): four consecutive columns (W = 4, 16-byte
+// loads of dy and c, one 8-byte store of dyh per token; d_out % 4 == 0) or one
+// column (W = 1), and the 16 tokens of one half of a block of 32; the two
+// halves of a block are adjacent lanes, whose sums are added through a lane
+// exchange (addition commutes, so either lane's sum has the same bits).  Every
+// value of dy and c a thread needs is loaded before any is used.
+template <int W, bool FULL>
+__device__ __forceinline__ void dyc_half(const DycArgs &q, int64_t b, int hk, int64_t n0, bool real) {
 #pragma clang fp contract(off)
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= q.N) return;
-    const float *__restrict__ dy = q.dy;
-    const float *__restrict__ c = q.c;
-    _Float16 *__restrict__ dyh = q.dyh;
-    const bool real = n < q.d_out;
-    const float f = real ? q.h[n] : 0.0f;
-    const int64_t hn = perm4((int)n);  // n < 2^30
-    for (int64_t b = blockIdx.y; b < q.blocks; b += gridDim.y) {
-        float half[2];
+    typedef float fw __attribute__((ext_vector_type(W)));
+    typedef _Float16 hw __attribute__((ext_vector_type(W)));
+    // rows of this half: 32b + 8(r/4) + 4hk + r%4; FULL: all 16 below M.  The
+    // loads are unconditional (padding columns read column 0 and rows past M
+    // read row M-1, then the values are replaced by 0), so they need no branches
+    // and go out together.
+    const int64_t nc = real ? n0 : 0;
+    const int64_t t0 = 32 * b + 4 * hk;
+    _Float16 *dyh = q.dyh + t0 * q.ldh + n0;
+    fw e[16], v[16];
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk) {
-            float e[16], v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t t = 32 * b + 8 * (r >> 2) + 4 * hk + (r & 3);
-                const bool live = real && t < q.M;
-                e[r] = live ? dy[t * q.d_out + n] : 0.0f;
-                v[r] = live ? c[t * q.d_out + n] : 0.0f;
-            }
-            float psum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t t = 32 * b + 8 * (r >> 2) + 4 * hk + (r & 3);
-                if (t < q.M) {
-                    if (real) psum = psum + e[r] * v[r];
-                    dyh[t * q.ldh + hn] = (_Float16)((e[r] * f) * q.gs);
-                }
-            }
-            half[hk] = psum;
-        }
-        if (real) q.part[b * q.d_out + n] = half[0] + half[1];
+    for (int r = 0; r < 16; ++r) {
+        const int64_t dt = 8 * (r >> 2) + (r & 3);
+        const bool live = real && (FULL || t0 + dt < q.M);
+        const int64_t t = FULL ? t0 + dt : (t0 + dt < q.M ? t0 + dt : q.M - 1);
+        const fw ev = *reinterpret_cast<const fw *>(q.dy + t * q.d_out + nc);
+        const fw cv = *reinterpret_cast<const fw *>(q.c + t * q.d_out + nc);
+        e[r] = live ? ev : fw{};
+        v[r] = live ? cv : fw{};
     }
+    const fw hf = *reinterpret_cast<const fw *>(q.h + nc);
+    const fw f = real ? hf : fw{};
+    fw psum{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t dt = 8 * (r >> 2) + (r & 3);
+        if (FULL || t0 + dt < q.M) {
+            psum = psum + e[r] * v[r];
+            const fw o = (e[r] * f) * q.gs;
+            if constexpr (W == 4) {
+                const hw out = {(_Float16)o[0], (_Float16)o[2], (_Float16)o[1], (_Float16)o[3]};  // perm4 order
+                *reinterpret_cast<hw *>(dyh + dt * q.ldh) = out;
+            } else {
+                dyh[dt * q.ldh + (perm4((int)n0) - n0)] = (_Float16)o[0];
+            }
+        }
+    }
+    fw other;
+#pragma unroll
+    for (int i = 0; i < W; ++i) other[i] = __shfl_xor(psum[i], 1);
+    if (real && hk == 0) *reinterpret_cast<fw *>(q.part + b * q.d_out + n0) = psum + other;
+}
+
+template <int W>
+__global__ __launch_bounds__(256) void blr_dyc_kernel(DycArgs q) {
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int hk = (int)(tid & 1);
+    const int64_t groups = q.N / W;
+    const int64_t n0 = ((tid >> 1) % groups) * W;
+    const int64_t b = (tid >> 1) / groups;
+    const bool real = n0 < q.d_out;  // d_out % W == 0: the group is all real or all padding
+    if (b >= q.blocks) return;       // whole lane pairs leave together
+    // blocks of 32 tokens below M take the path without per-token checks
+    if (32 * b + 32 <= q.M)
+        dyc_half<W, true>(q, b, hk, n0, real);
+    else
+        dyc_half<W, false>(q, b, hk, n0, real);
 }
 
 // out[n] = f32(out[n] + f32(sum over row blocks b in order of part[b][n])) for the
@@ -361,8 +390,15 @@ hipError_t launch_blr_backward_saved(const BlrBwdPlan &pb, const uint32_t *bits_
     q.dyh = reinterpret_cast<_Float16 *>(ws + pb.off_dyh);
     q.part = reinterpret_cast<float *>(ws + pb.off_part_dh);
     q.M = pl.M, q.d_out = pl.d_out, q.N = pb.kpado, q.ldh = pb.kpado, q.blocks = pb.blocks, q.gs = gs;
-    const unsigned gy = (unsigned)(pb.blocks < 65535 ? pb.blocks : 65535);
-    blr_dyc_kernel<<<dim3((unsigned)((pb.kpado + 255) / 256), gy), dim3(256), 0, s>>>(q);
+    // four columns per thread when rows of dy and c are 16-byte aligned
+    const bool vec = pl.d_out % 4 == 0 && ((reinterpret_cast<uintptr_t>(dy) | reinterpret_cast<uintptr_t>(c) |
+                                             reinterpret_cast<uintptr_t>(h)) & 15) == 0;
+    const int64_t threads = 2 * pb.blocks * (pb.kpado / (vec ? 4 : 1));
+    const unsigned wgs = (unsigned)((threads + 255) / 256);
+    if (vec)
+        blr_dyc_kernel<4><<<dim3(wgs), dim3(256), 0, s>>>(q);
+    else
+        blr_dyc_kernel<1><<<dim3(wgs), dim3(256), 0, s>>>(q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return backward_tail(pb, bits_u, bits_v, l, g, x, a, dx, dh, dl, dg, gs, ws, accumulate_dx,
