@@ -601,7 +601,20 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                 const int gn = n0 + wn * WTN + nb * 32 + lrow;
                 const int mblk = m0 + wm * WTM + mb * 32;  // first row of this 32-row block
                 const bool col = gn < p.N, real = gn < p.nrowf;
-                const float f = real ? p.rowf[gn] : 0.0f;
+                // the operands this lane reads (E, the old C of kEpiBwdDxAcc, the
+                // factor), loaded before any is used, unconditionally from clamped
+                // places (column 0 for padding columns, row M-1 past M), so they
+                // go out together rather than one per output
+                const int gnc = real ? gn : 0;
+                const float f = real ? p.rowf[gnc] : 0.0f;
+                float ev[16], cv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = mblk + 8 * (r >> 2) + 4 * hk + (r & 3);
+                    const int64_t rowc = gm < p.M ? gm : p.M - 1;
+                    ev[r] = p.ea[rowc * p.ldea + gnc];
+                    if constexpr (EPI == kEpiBwdDxAcc) cv[r] = p.C[rowc * p.ldc + gnc];
+                }
                 float psum = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -609,21 +622,20 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                     if (gm < p.M && col) {
                         const float v = acc[mb][nb][r];
                         const int64_t row = (int64_t)gm;
+                        const float e = real ? ev[r] : 0.0f;
                         if constexpr (EPI == kEpiBwdC) {
-                            const float e = real ? p.ea[row * p.ldea + gn] : 0.0f;
                             psum = psum + e * v;
                             p.Ch[row * p.ldch + perm4(gn)] = (_Float16)((e * f) * p.gs);
                         } else if constexpr (EPI == kEpiBwdDb) {
                             const float w = v * p.alpha;
-                            const float e = real ? p.ea[row * p.ldea + gn] : 0.0f;
                             psum = psum + e * w;
                             p.Ch[row * p.ldch + perm32(gn)] = (_Float16)((w * f) * p.gs);
                         } else {
                             const float w = v * p.alpha;
-                            psum = psum + p.ea[row * p.ldea + gn] * w;
+                            psum = psum + e * w;
                             float *c = p.C + row * p.ldc + gn;
                             if constexpr (EPI == kEpiBwdDx) *c = f * w;
-                            else *c = *c + f * w;
+                            else *c = cv[r] + f * w;
                         }
                     }
                 }
@@ -652,6 +664,16 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             const int hn = PERM_OUT ? perm32(gn) : gn;  // column of the f16 output
             if constexpr (EPI == kEpiScale) rf = p.alpha;
             float *C = p.C;
+            // accumulating epilogues: the old values of this lane's outputs, loaded
+            // together before any is written (rows past M read row M-1)
+            float cprev[16];
+            if constexpr (ACC) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
+                    cprev[r] = C[(int64_t)(gm < p.M ? gm : p.M - 1) * p.ldc + gn];
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
@@ -665,9 +687,8 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                     } else if constexpr (ACC) {
                         // two roundings: the product must not be fused into the sum
 #pragma clang fp contract(off)
-                        float *c = C + (int64_t)gm * p.ldc + gn;
                         const float prod = rf * v;
-                        *c = *c + prod;
+                        C[(int64_t)gm * p.ldc + gn] = cprev[r] + prod;
                     } else if constexpr (EPI == kEpiStoreNT) {
                         __builtin_nontemporal_store(v, &C[(int64_t)gm * p.ldc + gn]);
                     } else
