@@ -32,11 +32,14 @@ bool skinny_fits(const DevWeight &w, int64_t M);
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s);
 
 // Binary low-rank forward.  Workspace carve-up is computed by blr_plan: the
-// f16 operand f16(l.a) [M][kpad2] that GEMM1 writes and GEMM2 reads.
+// f16 operand f16(l.a) [M][kpad2] that GEMM1 writes and GEMM2 reads, and, when
+// GEMM1's contraction is split over ksplit1 workgroups per tile, their partial
+// products [ksplit1][M][kpad2] (f32).
 struct BlrPlan {
     int64_t M, d_in, d_out, r;
     int64_t kpad1, kpad2;        // contraction lengths of GEMM1 (d_in, padded) and GEMM2 (r, padded)
-    size_t off_al, total;
+    int64_t ksplit1;             // GEMM1's workgroups per output tile along d_in (1: not split)
+    size_t off_al, off_part1, total;
 };
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 // Binary low-rank backward: the forward's carve-up, then the backward's buffers.

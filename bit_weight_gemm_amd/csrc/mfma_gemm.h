@@ -87,8 +87,11 @@ struct GemmArgs {
     float *Cs;               // kEpiRowScaleSave / kEpiRowScaleAccSave: the product itself, [M][ldcs]
     int64_t ldcs;
     int M, N, K;             // true sizes; K bounds the A loads
-    int Kloop;               // k range of one workgroup: a multiple of the steps (codes are padded)
+    int Kloop;               // k range of one output tile: a multiple of the steps (codes are padded)
     int tiles_n;             // number of BN tiles along N
+    int ksplit;              // workgroups per output tile along K (0 or 1: one), each taking
+                             // Kloop/ksplit (a multiple of the steps); kEpiStore only
+    int64_t cks;             // kEpiStore with ksplit > 1: chunk j of K stores its partial tile at C + j*cks
 };
 
 // LDS has 64 four-byte banks on gfx950: a 16-byte read serves 16 lanes per
@@ -202,9 +205,14 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // Tile order: the hardware deals workgroups round-robin to the 8 XCDs; remap
     // so each XCD gets a contiguous run of tiles, and within the run walk N
     // first, so the workgroups sharing an A row-block share one XCD's L2.
+    // With K split over workgroups, the chunks of one tile are adjacent in that
+    // order, so they share an XCD too.
     const int tiles = gridDim.x;
     int tile = blockIdx.x;
     if ((tiles & 7) == 0) tile = (tile & 7) * (tiles >> 3) + (tile >> 3);
+    const int ksp = EPI == kEpiStore && p.ksplit > 1 ? p.ksplit : 1;
+    const int kchunk = tile % ksp;
+    tile /= ksp;
     const int m0 = (tile / p.tiles_n) * BM;
     const int n0 = (tile % p.tiles_n) * BN;
 
@@ -349,9 +357,12 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
 #pragma unroll
                 for (int rr = 0; rr < TRPT; ++rr) {
                     const int k = k0 + tid + rr * T;
+                    // one base offset plus 4w: the compiler merges the TW adjacent
+                    // words into 16-byte loads (a lane per contraction row, so each
+                    // load instruction touches one cache line per lane)
+                    const int off = (k * (int)p.ldb + (n0 >> 5)) * 4;
 #pragma unroll
-                    for (int w = 0; w < TW; ++w)
-                        treg[st][rr][w] = __builtin_amdgcn_raw_buffer_load_b32(brsrc, (k * (int)p.ldb + (n0 >> 5) + w) * 4, 0, 0);
+                    for (int w = 0; w < TW; ++w) treg[st][rr][w] = __builtin_amdgcn_raw_buffer_load_b32(brsrc, off + 4 * w, 0, 0);
                 }
             }
         }
@@ -490,8 +501,9 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // which every wave finished before the barrier that ended step t-1.  The
     // step count is a multiple of BDEPTH, so the loop is branch-free; loads and
     // stores past the end use clamped addresses and are never read.
-    const int nsteps = p.Kloop / SK;
-    auto clampk = [&](int t) { return (t < nsteps ? t : nsteps - 1) * SK; };
+    const int nsteps = p.Kloop / (SK * ksp);
+    const int kbeg = kchunk * nsteps * SK;  // this workgroup's chunk of K
+    auto clampk = [&](int t) { return kbeg + (t < nsteps ? t : nsteps - 1) * SK; };
 #pragma unroll
     for (int st = 0; st < BDEPTH; ++st) {
         if (st < ASTG) load_a(st, clampk(st));
@@ -663,7 +675,7 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             if constexpr (HALF_OUT) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
             const int hn = PERM_OUT ? perm32(gn) : gn;  // column of the f16 output
             if constexpr (EPI == kEpiScale) rf = p.alpha;
-            float *C = p.C;
+            float *C = p.C + (EPI == kEpiStore ? kchunk * p.cks : 0);
             // accumulating epilogues: the old values of this lane's outputs, loaded
             // together before any is written (rows past M read row M-1)
             float cprev[16];
@@ -705,7 +717,7 @@ template <int BM, int BN, int WM, int WN, int WK, int STAGES, int AMODE, bool SC
 inline hipError_t run_gemm(GemmArgs p, hipStream_t s) {
     p.tiles_n = (int)((p.N + BN - 1) / BN);  // kBCodes: tiles_n * BN <= Npad, so B rows stay in bounds
     const int64_t tiles_m = (p.M + BM - 1) / BM;
-    const int64_t tiles = tiles_m * p.tiles_n;
+    const int64_t tiles = tiles_m * p.tiles_n * (EPI == kEpiStore && p.ksplit > 1 ? p.ksplit : 1);
     mfma_gemm_kernel<BM, BN, WM, WN, WK, STAGES, BDEPTH, AMODE, SCALED, EPI, ASTG, KSUB, BMODE>
         <<<dim3((unsigned)tiles), dim3(WM * WN * WK * 64), 0, s>>>(p);
     return hipGetLastError();

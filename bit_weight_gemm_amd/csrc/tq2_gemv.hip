@@ -186,7 +186,10 @@ __global__ __launch_bounds__(256 * Q) void gemv_mt_kernel(const uint32_t *__rest
                                                           const float *__restrict__ x, float *__restrict__ y, int N,
                                                           int K) {
     __shared__ float red[4 * Q][4][MT];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is the same on every lane: read it into a scalar register,
+    // so the row and group offsets below are scalar arithmetic and each load
+    // adds only the lane's 32-bit offset to a scalar base
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int quad = wave >> 2, kwave = wave & 3;
     const int row0 = blockIdx.x * 4 * Q;  // first weight row of the workgroup
     const int n0 = row0 + 4 * quad;       // this wave's row quad (< Npad: padded rows are code 1)

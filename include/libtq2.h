@@ -126,8 +126,9 @@ int tq2_dequant(const tq2_weight *w, float *w_out, void *stream);
  * [M][d_in]; y: device f32 [M][d_out], overwritten, 16-byte aligned, must not
  * overlap the inputs.  Requires d_in >= 1, d_out >= 1, r >= 32, r % 32 == 0, M >= 0
  * (M == 0 is a no-op), and each bitmap with 512 more rows under 2 GB
- * ((rows + 512) * r/8 < 2^31 bytes).  The f16(a*l) intermediate lives in a workspace that the
- * library owns: one grow-only device buffer per (device, stream), allocated on
+ * ((rows + 512) * r/8 < 2^31 bytes).  The f16(a*l) intermediate (and, for sizes
+ * where the first product's contraction is split over workgroups, its f32
+ * partial products) lives in a workspace that the library owns: one grow-only device buffer per (device, stream), allocated on
  * first use and enlarged (never shrunk) when a call needs more, kept until the
  * process ends (tq2_workspace_allocs counts these allocations).  The page's
  * layer likewise keeps its staging buffers in a scratch object it reuses.

@@ -106,7 +106,13 @@ def test_workspace_counter_starts_at_zero_without_a_device(L):
 
 
 def test_workspace_size_rules(L):
-    assert bw.blr_workspace_size(512, 4096, 4096, 1024) == 512 * 1024 * 2   # f16(l.a) [M][r]
+    # f16(l.a) [M][r], then the partial products of a over two chunks of d_in (f32)
+    assert bw.blr_workspace_size(512, 4096, 4096, 1024) == 512 * 1024 * 2 + 2 * 512 * 1024 * 4
+    assert bw.blr_workspace_size(1, 4096, 4096, 1024) == 1024 * 2   # too few tiles to split d_in
+    # fewer tiles: four chunks; d_in padded to 1024: two chunks; padded to 1536: not split
+    assert bw.blr_workspace_size(128, 4096, 4096, 1024) == 128 * 1024 * 2 + 4 * 128 * 1024 * 4
+    assert bw.blr_workspace_size(512, 1000, 4096, 1024) == 512 * 1024 * 2 + 2 * 512 * 1024 * 4
+    assert bw.blr_workspace_size(512, 1536, 4096, 1024) == 512 * 1024 * 2
     assert bw.blr_workspace_size(1, 4096, 4096, 1000) == 0     # r % 32 != 0
     assert bw.blr_workspace_size(1, 0, 4096, 1024) == 0        # d_in < 1
     assert bw.blr_workspace_size(-1, 8, 8, 32) == 0            # M < 0

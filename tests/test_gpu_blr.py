@@ -73,6 +73,16 @@ def test_blr_ragged_shapes(torch, m, d_in, d_out, r):
     _check(wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=20 + m), f"ragged {m}x{d_in}x{d_out}x{r}")
 
 
+@pytest.mark.parametrize("m,d_in,d_out,r", [(300, 4096, 200, 1024), (520, 1000, 96, 1024), (1024, 2048, 64, 256),
+                                            (128, 4096, 300, 1024)])
+def test_blr_split_contraction(torch, m, d_in, d_out, r):
+    """Sizes whose first product splits d_in over workgroups and adds the chunks' partial
+    products in a last launch: two chunks with ragged M and vector x loads; two chunks with a
+    d_in tail and scalar x loads; two chunks with r = 256; four chunks."""
+    _check(wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=50 + m), f"split {m}x{d_in}x{d_out}x{r}",
+           count=2048)
+
+
 def test_blr_many_tokens(torch):
     """Enough tokens that the first product takes its large tiles (4100 x 1024 outputs)."""
     _check(wl.blr_inputs(m=4100, d_in=256, d_out=96, r=1024, index=41), "many tokens", count=2048)
