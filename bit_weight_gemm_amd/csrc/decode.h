@@ -58,6 +58,35 @@ __device__ __forceinline__ void word_m1(uint32_t w, uint32_t magic, h2 out[8]) {
     out[7] = pair_m1<4>(w6, magic);
 }
 
+// The same decode with its constants in scalar registers, for kernels that
+// decode each word once (so nothing is gained by keeping per-position constants
+// in vector registers): v_bfi_b32 takes the mask from an SGPR and the word and
+// the 0x6400 pattern from VGPRs, and v_pk_fma_f16 takes the factor 4^-P and the
+// offset -(2^(10-2P) + 1) from the low and high halves of one SGPR (op_sel).
+constexpr uint32_t f16_bits(float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); }
+template <int P>
+__device__ __forceinline__ h2 pair_m1_s(uint32_t w, uint32_t magic) {
+    static_assert(P >= 0 && P <= 4, "pair position must lie in the f16 fraction");
+    constexpr uint32_t mask = 0x00030003u << (2 * P);
+    constexpr uint32_t k = f16_bits(1.0f / float(1 << (2 * P))) | (f16_bits(-float((1 << (10 - 2 * P)) + 1)) << 16);
+    uint32_t t, r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(t) : "s"(mask), "v"(w), "v"(magic));
+    asm("v_pk_fma_f16 %0, %1, %2, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(t), "s"(k));
+    return as_h2(r);
+}
+static_assert(f16_bits(1.0f / 256.0f) == 0x1C00u && f16_bits(-1025.0f) == 0xE401u, "f16 constants");
+__device__ __forceinline__ void word_m1_s(uint32_t w, uint32_t magic, h2 out[8]) {
+    out[0] = pair_m1_s<0>(w, magic);
+    out[1] = pair_m1_s<1>(w, magic);
+    out[2] = pair_m1_s<2>(w, magic);
+    out[3] = pair_m1_s<3>(w, magic);
+    out[4] = pair_m1_s<4>(w, magic);
+    const uint32_t w6 = w >> 6;
+    out[5] = pair_m1_s<2>(w6, magic);
+    out[6] = pair_m1_s<3>(w6, magic);
+    out[7] = pair_m1_s<4>(w6, magic);
+}
+
 // The 4 pairs of one half-group (elements 8h..8h+7) as an MFMA operand of 8
 // consecutive k: shift the word by 8h so the wanted pairs sit at positions 0..3.
 __device__ __forceinline__ h8 half_group_m1(uint32_t w, int h, uint32_t magic) {
