@@ -3,8 +3,10 @@
 Callers that capture their work in graphs (the bench does, and so do serving
 loops) need every call to be capturable once warmed up: no allocation, no
 host synchronisation and no memset node.  A graph holding ternary GEMMs on
-both paths, a binary low-rank forward on the library's workspace, one on the
-fixed scratch (blr_forward_noalloc) and the backward from saved activations is
+both paths, a binary low-rank forward on the library's workspace (at a size
+whose first product is one launch, and at one whose contraction is split over
+workgroups with a launch that adds the chunks), one on the fixed scratch
+(blr_forward_noalloc) and the backward from saved activations is
 replayed several times, with other eager library work and synchronisations in
 between, and every replay must give the eager results bit for bit; after the
 inputs are overwritten in place, a replay must give the eager results on the
@@ -43,11 +45,16 @@ def test_graph_replays_match_eager(torch):
     grads = [torch.zeros((1, m), device="cuda") for m in (256, 128, 384)]
     dx = torch.empty((70, 384), device="cuda")
     P = lambda t: t[None]  # noqa: E731  (one path)
+    # first product split four ways over d_in (10 x 4 tiles of 32 x 128)
+    d2 = wl.blr_inputs(m=300, d_in=2048, d_out=256, r=512, index=39)
+    b2 = [bits_dev(d2["bits_u"]), bits_dev(d2["bits_v"])] + [to_dev(d2[key]) for key in ("h", "l", "g", "x")]
+    y2 = torch.empty((300, 256), device="cuda")
 
     def work(s):
         bw.tq2_gemm_path(w, x1, y1, bw.TQ2_PATH_F32, stream=s)
         bw.tq2_gemm_path(w, x100, y100, bw.TQ2_PATH_MFMA, stream=s)
         bw.blr_forward(bu, bv, h, l, g, xb, yb, stream=s)
+        bw.blr_forward(*b2, y2, stream=s)
         bw._check(bw.lib().blr_forward_noalloc(
             bw._dev(bu, torch.int32, "bu"), bw._dev(bv, torch.int32, "bv"), bw._dev(h, torch.float32, "h"),
             bw._dev(l, torch.float32, "l"), bw._dev(g, torch.float32, "g"), bw._dev(xb, torch.float32, "x"),
@@ -55,7 +62,7 @@ def test_graph_replays_match_eager(torch):
         bw.blr_forward_paths_save(P(bu), P(bv), P(h), P(l), P(g), xb, ys, saved, stream=s)
         bw.blr_backward_paths_saved(P(bu), P(bv), P(h), P(l), P(g), xb, dy, *grads, saved, dx=dx, stream=s)
 
-    outs = (y1, y100, yb, yn, ys, dx)
+    outs = (y1, y100, yb, yn, ys, dx, y2)
 
     def eager():
         for t in grads:
@@ -99,6 +106,7 @@ def test_graph_replays_match_eager(torch):
     x1.copy_(to_dev(wl.random_x(1, k, 36)))
     x100.copy_(to_dev(wl.random_x(100, k, 37)))
     xb.copy_(to_dev(wl.random_x(70, 384, 38)))
+    b2[5].copy_(to_dev(wl.random_x(300, 2048, 40)))
     torch.cuda.synchronize()
     got = replay()
     want2 = eager()

@@ -99,8 +99,10 @@ def test_pool_grows_once_for_a_larger_call_and_per_stream(torch):
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-def test_library_and_caller_workspaces_give_the_same_bits(torch):
-    d = wl.blr_inputs(m=70, d_in=384, d_out=256, r=128, index=62)
+@pytest.mark.parametrize("m,d_in,d_out,r", [(70, 384, 256, 128), (300, 2048, 256, 512)])
+def test_library_and_caller_workspaces_give_the_same_bits(torch, m, d_in, d_out, r):
+    # the second size splits the first product's contraction over workgroups
+    d = wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=62)
     dev = _blr_dev(d)
     a = bw.blr_forward(*dev)
     b = bw.blr_forward_ws(*dev)
