@@ -98,31 +98,23 @@ __device__ __forceinline__ h8 half_group_m1(uint32_t w, int h, uint32_t magic) {
 
 // ---- sign bits (binary low-rank layer: a set bit is +1, a clear bit -1)
 //
-// (2b - 1) for the two bits at positions P and 16+P of `t` (1 <= P <= 9): the
-// bits go into the f16 fraction of 0x6400 (1024 + b*2^P), and one packed fused
-// multiply-add by 2^(1-P) minus (2^(11-P) + 1) leaves 2b - 1.  Every value is a
-// small integer or a power-of-two multiple of one, so the result is exact.
-template <int P>
-__device__ __forceinline__ h2 pair_sign(uint32_t t, uint32_t magic) {
-    static_assert(P >= 1 && P <= 9, "the constant 2^(11-P) + 1 must be an f16 integer");
-    constexpr uint32_t mask = 0x00010001u << P;
-    const uint32_t v = (t & mask) | (magic & ~mask);
-    constexpr float scl = 2.0f / float(1 << P);
-    constexpr float off = -float((1 << (11 - P)) + 1);
-    const h2 vs = {(_Float16)scl, (_Float16)scl};
-    const h2 vo = {(_Float16)off, (_Float16)off};
-    return __builtin_elementwise_fma(as_h2(v), vs, vo);
-}
+// In f16, +1 (0x3C00) and -1 (0xBC00) differ only in the sign bit.  With the
+// two bits of a pair rotated to positions 15 and 31 (the halves' sign bits),
+// keeping just those two bits and flipping -1 by them gives (2b - 1) in each
+// half: one rotation and one three-input bitwise operation (v_bitop3_b32) per
+// pair, the values exact.
+__device__ __forceinline__ uint32_t sign_pair15(uint32_t t) { return (t & 0x80008000u) ^ 0xBC00BC00u; }
+// `w` rotated right by `s` (mod 32)
+__device__ __forceinline__ uint32_t rotr(uint32_t w, uint32_t s) { return __builtin_amdgcn_alignbit(w, w, s & 31u); }
 
 // Octet o (0..3) of a word of 32 sign bits along k as an MFMA operand: the eight
 // elements are k = 4o+i and 4o+i+16 for i = 0..3, in the order 4o, 4o+16, 4o+1,
-// 4o+17, ...  A rotation by 4o-1 puts bit 4o+i at position i+1 and bit 4o+i+16 at
-// i+17 for all four pairs at once.  The A operand must hold the same k order
-// (perm32 below).
-__device__ __forceinline__ h8 sign_octet(uint32_t w, int o, uint32_t magic) {
-    const uint32_t t = __builtin_amdgcn_alignbit(w, w, (uint32_t)(4 * o - 1) & 31u);
-    const h2 p0 = pair_sign<1>(t, magic), p1 = pair_sign<2>(t, magic), p2 = pair_sign<3>(t, magic),
-             p3 = pair_sign<4>(t, magic);
+// 4o+17, ...  Pair i (bits 4o+i and 4o+i+16) is rotated right by 4o+i-15 to the
+// sign bits.  The A operand must hold the same k order (perm32 below).
+__device__ __forceinline__ h8 sign_octet(uint32_t w, int o) {
+    const uint32_t s = (uint32_t)(4 * o + 17);
+    const h2 p0 = as_h2(sign_pair15(rotr(w, s))), p1 = as_h2(sign_pair15(rotr(w, s + 1))),
+             p2 = as_h2(sign_pair15(rotr(w, s + 2))), p3 = as_h2(sign_pair15(rotr(w, s + 3)));
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
@@ -134,14 +126,12 @@ __host__ __device__ inline int perm32(int k) {
 // Eight sign bits of one column from eight contraction rows, as the column's byte
 // (bit p) of rows k0..k3 in `lo` and k4..k7 in `hi` (row r in byte r), as an MFMA
 // operand in the k order k0, k2, k1, k3, k4, k6, k5, k7: rows two apart sit 16 bits
-// apart, so one rotation by p-1 puts rows k0 and k2 at bits 1 and 17 and rows k1
-// and k3 at bits 9 and 25, two pairs per word.  The A operand must hold the same
-// k order (perm4 below).
-__device__ __forceinline__ h8 sign_rows8(uint32_t lo, uint32_t hi, int p, uint32_t magic) {
-    const uint32_t sh = (uint32_t)(p - 1) & 31u;
-    const uint32_t tl = __builtin_amdgcn_alignbit(lo, lo, sh), th = __builtin_amdgcn_alignbit(hi, hi, sh);
-    const h2 p0 = pair_sign<1>(tl, magic), p1 = pair_sign<9>(tl, magic), p2 = pair_sign<1>(th, magic),
-             p3 = pair_sign<9>(th, magic);
+// apart, so rotating right by p-15 puts rows k0 and k2 on the sign bits, and by
+// p-7 rows k1 and k3.  The A operand must hold the same k order (perm4 below).
+__device__ __forceinline__ h8 sign_rows8(uint32_t lo, uint32_t hi, int p) {
+    const uint32_t s0 = (uint32_t)(p + 17), s1 = (uint32_t)(p + 25);
+    const h2 p0 = as_h2(sign_pair15(rotr(lo, s0))), p1 = as_h2(sign_pair15(rotr(lo, s1))),
+             p2 = as_h2(sign_pair15(rotr(hi, s0))), p3 = as_h2(sign_pair15(rotr(hi, s1)));
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 

@@ -472,14 +472,14 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
                         if constexpr (SCALED) b[nb] = b[nb] * dv[nb];
                     } else if constexpr (BMODE == kBSign) {
                         // octet 2*(j&1)+hk of the slice's word j/2 (k order perm32)
-                        b[nb] = sign_octet(j < 2 ? sw2[nb].x : sw2[nb].y, 2 * (j & 1) + hk, magic);
+                        b[nb] = sign_octet(j < 2 ? sw2[nb].x : sw2[nb].y, 2 * (j & 1) + hk);
                     } else {
                         // column n, contraction rows sl*64 + 16j + 8hk .. +7 (k order perm4)
                         const int n = wn * WTN + nb * 32 + lrow;
                         const uint2 v = *reinterpret_cast<const uint2 *>(
                             reinterpret_cast<const unsigned char *>(&Bsm[st][0]) + (n >> 3) * TSTRIDE +
                             sl * 64 + 16 * j + 8 * hk);
-                        b[nb] = sign_rows8(v.x, v.y, n & 7, magic);
+                        b[nb] = sign_rows8(v.x, v.y, n & 7);
                     }
                 }
 #pragma unroll
