@@ -48,7 +48,7 @@ def tq2_bytes(n, k):
 
 KERNEL_SOURCES = {  # files whose content defines each timed kernel
     "gemv_mt_kernel": ["tq2_gemv.hip", "decode.h", "internal.h", "layout.h"],
-    "mfma_gemm_kernel": ["mfma_gemm.h", "mfma_gemm.hip", "decode.h", "internal.h", "layout.h"],
+    "mfma_gemm_kernel": ["mfma_gemm.h", "mfma_gemm.hip", "decode.h", "bitsign.h", "internal.h", "layout.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 256 << 20   # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE

@@ -32,6 +32,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "bitsign.h"
 #include "decode.h"
 #include "internal.h"
 
@@ -57,7 +58,7 @@ enum Epi { kEpiStore = 0, kEpiRowScale = 1, kEpiHalfScale = 2, kEpiRowScaleAcc =
 // for element (n, k), set = +1; kBSignT, a sign bitmap bits[k][ldb] with bit n%32
 // of word n/32 for element (n, k) (the contraction runs down its rows).  The sign
 // modes need the A operand's k order permuted within groups (perm32 for kBSign,
-// perm4 for kBSignT, see decode.h): each A producer writes that order.
+// perm4 for kBSignT, see bitsign.h): each A producer writes that order.
 enum BMode { kBCodes = 0, kBSign = 1, kBSignT = 2 };
 
 struct GemmArgs {
