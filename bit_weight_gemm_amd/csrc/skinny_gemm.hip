@@ -157,34 +157,30 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
         }
     }
 
-    // ---- add the waves' partial tiles in wave order (LDS reused after the barrier)
+    // ---- the waves' partial tiles added in wave order (LDS reused after the
+    // barrier).  Registers 4j..4j+3 of a block hold its rows 8j..8j+7, so only the
+    // first 4*ceil(M/8) registers hold rows below M: every wave leaves those in
+    // LDS, then the waves share the sums, each (block, register) added over the
+    // waves in wave order (the order of one wave adding the others, so the same
+    // bits), and store them.
     __syncthreads();
     float *red = reinterpret_cast<float *>(xs);
     auto at = [&](int w, int nb, int r) { return ((w * NBW + nb) * 16 + r) * 64 + lane; };
-    if (wave > 0) {
+    const int nreg = 4 * ((p.M + 7) / 8);  // 4 or 8 (M <= 16)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[at(wave - 1, nb, r)] = acc[nb][r];
-    }
+        for (int r = 0; r < 16; ++r)
+            if (r < nreg) red[at(wave, nb, r)] = acc[nb][r];  // wave-uniform
     __syncthreads();
-    if (wave > 0) return;
-#pragma unroll 1
-    for (int w = 1; w < WK; ++w)
+    for (int it = wave; it < NBW * nreg; it += WK) {  // wave-uniform
+        const int nb = it / nreg, r = it % nreg;
+        float v = red[at(0, nb, r)];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[nb][r] += red[at(w - 1, nb, r)];
-    // lane holds column lrow of each block, rows 8*(r/4) + 4*hk + r%4
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-        const int gn = col[nb];
-        if (gn >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int gm = 8 * (r >> 2) + 4 * hk + (r & 3);
-            if (gm < p.M) p.y[(int64_t)gm * p.N + gn] = acc[nb][r];
-        }
+        for (int w = 1; w < WK; ++w) v += red[at(w, nb, r)];
+        // lane holds column lrow of the block, rows 8*(r/4) + 4*hk + r%4
+        const int gm = 8 * (r >> 2) + 4 * hk + (r & 3), gn = n0 + 32 * nb + lrow;
+        if (gm < p.M && gn < p.N) p.y[(int64_t)gm * p.N + gn] = v;
     }
 }
 
@@ -245,7 +241,7 @@ hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M
     a.kb = (int)(w.K / kBlock);
     // Eight waves; wave w owns K/8, i.e. K/512 steps, in a multiple of the
     // prefetch depth D.  LDS: x as f16 (padded rows), later the waves' sums.
-    const size_t xb = (size_t)M * (w.K + 8) * 2, rb = (size_t)7 * 16 * 64 * 4;
+    const size_t xb = (size_t)M * (w.K + 8) * 2, rb = (size_t)8 * 16 * 64 * 4;
     const size_t lds = xb > rb ? xb : rb;
     const int64_t steps = w.K / 512;
     // one workgroup per CU: 64 columns per workgroup once 32-column ones would
