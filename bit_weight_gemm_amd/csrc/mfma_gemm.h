@@ -538,6 +538,17 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
     // acc1 + acc0 has the bits of acc0 + acc1.
     constexpr bool SPLIT = WK == 2 && (MB * NB) % (2 * RED_ROUNDS) == 0;
     constexpr int HALF = MB * NB / 2;
+    // Otherwise, for the forward epilogues of four or more groups (with two, the
+    // extra LDS round of group 0 costs more than the sharing saves: the split BLR
+    // first product 26.5 -> 26.7 us per layer), with all the groups' tiles fitting
+    // in LDS at once: every group leaves its whole partial tile there, then group g
+    // adds registers g*RPG .. g*RPG+RPG-1 of every block over the groups in group
+    // order (the order of group 0 adding the others, so the same bits) and stores
+    // those outputs itself, so the sums and the stores are shared by all waves.
+    constexpr bool BWDE = EPI == kEpiBwdC || EPI == kEpiBwdDb || EPI == kEpiBwdDx || EPI == kEpiBwdDxAcc;
+    constexpr bool DIST = !SPLIT && WK >= 4 && 16 % WK == 0 && !BWDE &&
+                          WK * NW * MB * NB * 1024 * 4 <= STAGES * BM * SK * 2;
+    constexpr int RPG = DIST ? 16 / WK : 16;  // accumulator registers each group finishes
     if constexpr (SPLIT) {
         constexpr int HPR = HALF / RED_ROUNDS;  // blocks each group hands over per round
         float *red = reinterpret_cast<float *>(&As[0][0]);
@@ -569,6 +580,24 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             }
             if (ro + 1 < RED_ROUNDS) __syncthreads();
         }
+    } else if constexpr (DIST) {
+        float *red = reinterpret_cast<float *>(&As[0][0]);
+        auto at = [&](int g, int b, int r) { return ((g * NW + wr) * (MB * NB) + b) * 1024 + r * 64 + lane; };
+#pragma unroll
+        for (int b = 0; b < MB * NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[at(wk, b, r)] = acc[b / NB][b % NB][r];
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < MB * NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (r / RPG != wk) continue;  // wave-uniform
+                float v = red[at(0, b, r)];
+#pragma unroll
+                for (int g = 1; g < WK; ++g) v += red[at(g, b, r)];
+                acc[b / NB][b % NB][r] = v;
+            }
     } else if constexpr (WK > 1) {
         // k groups 1..WK-1 leave their partial tiles in LDS (over the A tiles,
         // which the loop no longer reads); group 0 adds them in group order.
@@ -683,12 +712,14 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             if constexpr (ACC) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    if (DIST && r / RPG != wk) continue;  // another group stores it
                     const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                     cprev[r] = C[(int64_t)(gm < p.M ? gm : p.M - 1) * p.ldc + gn];
                 }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                if (DIST && r / RPG != wk) continue;  // another group stores it
                 const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (gm < p.M) {
                     const float v = acc[mb][nb][r];
