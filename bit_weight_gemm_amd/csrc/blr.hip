@@ -21,7 +21,7 @@ static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // enough workgroups stream the long K without splitting it; larger M takes
 // 128 x 128 tiles.
 constexpr int kBlrKPad = 512;          // GEMM1's K padding: whole pipeline rounds of either tile
-constexpr int kBlr2Step = 2 * 2 * BK;  // GEMM2: two k groups x 64, two stages
+constexpr int kBlr2Step = 2 * 2 * BK;  // GEMM2: 128-wide steps, two stages
 
 static bool blr_small_tiles(int64_t M, int64_t kpad2) { return ((M + 31) / 32) * (kpad2 / 64) < 2048; }
 
@@ -64,13 +64,16 @@ static hipError_t gemm_long_k(const GemmArgs &p, int64_t kpad, bool small, hipSt
     if (half_a && kpad % 1024 == 0) return run_gemm<32, 64, 1, 2, 4, 2, AMODE, false, EPI, 2, 1, 2, kBSignT>(p, s);
     return run_gemm<32, 64, 1, 2, 4, 2, AMODE, false, EPI, 2, 2, 1, kBSignT>(p, s);
 }
-// Products with the short contraction r (GEMM2, and the backward's dx'), B a
-// bitmap whose bits run along r: 64 x 128 tiles of eight waves (two k groups),
-// A loaded two steps ahead.
+// Products with the short contraction r (GEMM2, and the backward's c and dx'), B
+// a bitmap whose bits run along r: 64 x 128 tiles of eight waves (two row waves
+// by four column waves, one k group taking two 64-wide slices of each 128-wide
+// step), A loaded two steps ahead.  With only eight steps per tile, two k groups
+// (one slice each) cost more in their closing sums than their shorter loop saves
+// (GEMM2 at M=512, d_out=4096, r=1024: 10.6 against 10.85 us alone).
 template <int EPI>
 static hipError_t gemm_short_k(const GemmArgs &p, hipStream_t s) {
-    if (half_buf(p)) return run_gemm<64, 128, 1, 4, 2, 2, kAHalfBuf, false, EPI, 2, 2, 1, kBSign>(p, s);
-    return run_gemm<64, 128, 1, 4, 2, 2, kAHalf, false, EPI, 2, 2, 1, kBSign>(p, s);
+    if (half_buf(p)) return run_gemm<64, 128, 2, 4, 1, 2, kAHalfBuf, false, EPI, 2, 2, 2, kBSign>(p, s);
+    return run_gemm<64, 128, 2, 4, 1, 2, kAHalf, false, EPI, 2, 2, 2, kBSign>(p, s);
 }
 
 BlrPlan blr_plan(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
