@@ -30,14 +30,19 @@ static bool blr_small_tiles(int64_t M, int64_t kpad2) { return ((M + 31) / 32) *
 // multiple of 512.  With the small tiles a workgroup stages its 32 rows of x
 // (f32, multiplied by g and rounded to f16) over all of d_in; split two (or
 // four) ways over tiles twice as wide, it stages half (a quarter) of them for
-// the same MFMA work, and reads its bitmap rows in 16-byte pieces.  A last
-// launch adds the chunks' partial products in order (blr_g1_finish_kernel).  At
-// M=512, d_in=4096, r=1024 the product takes 13.5 us against 18.0 for the
-// unsplit small tiles.  Used where the small tiles would be used and the split
-// grid fills between half and two times the CUs.
+// the same MFMA work, and a last launch adds the chunks' partial products in
+// order (blr_g1_finish_kernel), which costs ~3 us per layer.  Measured per layer
+// call (unsplit / split, us) at d_in = 4096, r = 1024: M=128 22.4 / 19.3, M=256
+// 23.5 / 22.7, M=512 25.9 / 26.3, M=1024 44.9 / 42.6; at d_in = 2048, r = 512:
+// M=512 15.6 / 17.0, M=300 15.0 / 15.1.  So the split is used with d_in >= 4096
+// where the 32 x 64 tiles would not make exactly one full round of workgroups
+// (fewer than 192, or more than 256), and the split grid fills between half and
+// two times the CUs.
 constexpr int kG1SplitRound = 512;
 static int64_t gemm1_ksplit(int64_t M, int64_t kpad1, int64_t kpad2) {
-    if (!blr_small_tiles(M, kpad2) || kpad2 % 128 != 0) return 1;
+    if (!blr_small_tiles(M, kpad2) || kpad2 % 128 != 0 || kpad1 < 4096) return 1;
+    const int64_t unsplit = ((M + 31) / 32) * (kpad2 / 64);
+    if (unsplit >= 192 && unsplit <= 256) return 1;
     const int64_t tiles = ((M + 31) / 32) * (kpad2 / 128);
     for (int64_t ks = 2; ks <= 4; ks *= 2)
         if (kpad1 % (ks * kG1SplitRound) == 0 && tiles * ks >= 128 && tiles * ks <= 512) return ks;

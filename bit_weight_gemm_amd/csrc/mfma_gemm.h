@@ -694,7 +694,10 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
         for (int nb = 0; nb < NB; ++nb) {
             if (SPLIT && ((mb * NB + nb) < HALF) != (wk == 0)) continue;  // the partner group stores it
             const int gn = n0 + wn * WTN + nb * 32 + lrow;
-            if (gn >= p.N) continue;
+            constexpr bool PAIRS = EPI == kEpiHalfScaleP || EPI == kEpiStoreHalfP;
+            // (the paired f16 stores below exchange values between lanes, so no
+            // lane leaves before them; their columns are checked there)
+            if (!PAIRS && gn >= p.N) continue;
             float rf = 1.0f;
             constexpr bool SAVE = EPI == kEpiRowScaleSave || EPI == kEpiRowScaleAccSave;
             constexpr bool ACC = EPI == kEpiRowScaleAcc || EPI == kEpiRowScaleAccSave;
@@ -704,6 +707,40 @@ __global__ __launch_bounds__(WM *WN *WK * 64) void mfma_gemm_kernel(GemmArgs p) 
             constexpr bool PERM_OUT = EPI == kEpiHalfScaleP || EPI == kEpiStoreHalfP;
             if constexpr (HALF_OUT) rf = gn < p.nrowf ? p.rowf[gn] : 0.0f;
             const int hn = PERM_OUT ? perm32(gn) : gn;  // column of the f16 output
+            if constexpr (PAIRS) {
+                // f16(rf*v) in the perm32 order, where columns n and n+16 of a row
+                // are adjacent: for registers r, r+1 (rows R, R'), lanes 16..31 of
+                // each 32-lane half swap their row-R value for lanes 0..15's row-R'
+                // value (v_permlane16_swap), so each lane stores one 4-byte pair of
+                // one row (a row's 32 outputs are 64 contiguous bytes)
+                _Float16 hout[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    hout[r] = (_Float16)0.0f;
+                    if (DIST && r / RPG != wk) continue;  // another group stores it
+                    const int gm = m0 + wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * hk + (r & 3);
+                    const float v = acc[mb][nb][r];
+                    if constexpr (EPI == kEpiStoreHalfP)
+                        if (gm < p.M && gn < p.nrowf) p.C[(int64_t)gm * p.ldc + gn] = v;
+                    hout[r] = (_Float16)(rf * v);
+                }
+                const int cb = (gn & ~31) + (lrow & 15);  // the pair's first column
+                const bool upper = (lrow & 16) != 0;
+                const int64_t ldh = EPI == kEpiStoreHalfP ? p.ldch : p.ldc;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    if (DIST && r / RPG != wk) continue;  // wave-uniform (RPG is even)
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint16_t, hout[r]),
+                                                                     __builtin_bit_cast(uint16_t, hout[r + 1]), false, false);
+                    // lanes 0..15: row R, columns cb and cb+16; lanes 16..31: row R', the same columns
+                    const int rr = upper ? r + 1 : r;
+                    const int gm = m0 + wm * WTM + mb * 32 + 8 * (rr >> 2) + 4 * hk + (rr & 3);
+                    if (gm < p.M && cb + 16 < p.N)
+                        *reinterpret_cast<uint32_t *>(&p.Ch[(int64_t)gm * ldh + perm32(cb)]) =
+                            (uint32_t)sw[0] | ((uint32_t)sw[1] << 16);
+                }
+                continue;
+            }
             if constexpr (EPI == kEpiScale) rf = p.alpha;
             float *C = p.C + (EPI == kEpiStore ? kchunk * p.cks : 0);
             // accumulating epilogues: the old values of this lane's outputs, loaded

@@ -106,13 +106,15 @@ def test_workspace_counter_starts_at_zero_without_a_device(L):
 
 
 def test_workspace_size_rules(L):
-    # f16(l.a) [M][r], then the partial products of a over two chunks of d_in (f32)
-    assert bw.blr_workspace_size(512, 4096, 4096, 1024) == 512 * 1024 * 2 + 2 * 512 * 1024 * 4
+    # f16(l.a) [M][r] (the first product's 32 x 64 tiles make one full round: not split)
+    assert bw.blr_workspace_size(512, 4096, 4096, 1024) == 512 * 1024 * 2
     assert bw.blr_workspace_size(1, 4096, 4096, 1024) == 1024 * 2   # too few tiles to split d_in
-    # fewer tiles: four chunks; d_in padded to 1024: two chunks; padded to 1536: not split
+    # then the partial products of a over the chunks of d_in (f32): four chunks at M=128,
+    # two at M=256 and M=1024; d_in below 4096: not split
     assert bw.blr_workspace_size(128, 4096, 4096, 1024) == 128 * 1024 * 2 + 4 * 128 * 1024 * 4
-    assert bw.blr_workspace_size(512, 1000, 4096, 1024) == 512 * 1024 * 2 + 2 * 512 * 1024 * 4
-    assert bw.blr_workspace_size(512, 1536, 4096, 1024) == 512 * 1024 * 2
+    assert bw.blr_workspace_size(256, 4096, 4096, 1024) == 256 * 1024 * 2 + 2 * 256 * 1024 * 4
+    assert bw.blr_workspace_size(1024, 4096, 4096, 1024) == 1024 * 1024 * 2 + 2 * 1024 * 1024 * 4
+    assert bw.blr_workspace_size(256, 2048, 4096, 1024) == 256 * 1024 * 2
     assert bw.blr_workspace_size(1, 4096, 4096, 1000) == 0     # r % 32 != 0
     assert bw.blr_workspace_size(1, 0, 4096, 1024) == 0        # d_in < 1
     assert bw.blr_workspace_size(-1, 8, 8, 32) == 0            # M < 0

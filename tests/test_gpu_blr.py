@@ -73,7 +73,7 @@ def test_blr_ragged_shapes(torch, m, d_in, d_out, r):
     _check(wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=20 + m), f"ragged {m}x{d_in}x{d_out}x{r}")
 
 
-@pytest.mark.parametrize("m,d_in,d_out,r", [(300, 4096, 200, 1024), (520, 1000, 96, 1024), (1024, 2048, 64, 256),
+@pytest.mark.parametrize("m,d_in,d_out,r", [(300, 4096, 200, 1024), (520, 4000, 96, 1024), (1024, 4096, 64, 256),
                                             (128, 4096, 300, 1024)])
 def test_blr_split_contraction(torch, m, d_in, d_out, r):
     """Sizes whose first product splits d_in over workgroups and adds the chunks' partial

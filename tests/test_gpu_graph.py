@@ -46,7 +46,7 @@ def test_graph_replays_match_eager(torch):
     dx = torch.empty((70, 384), device="cuda")
     P = lambda t: t[None]  # noqa: E731  (one path)
     # first product split four ways over d_in (10 x 4 tiles of 32 x 128)
-    d2 = wl.blr_inputs(m=300, d_in=2048, d_out=256, r=512, index=39)
+    d2 = wl.blr_inputs(m=300, d_in=4096, d_out=256, r=512, index=39)
     b2 = [bits_dev(d2["bits_u"]), bits_dev(d2["bits_v"])] + [to_dev(d2[key]) for key in ("h", "l", "g", "x")]
     y2 = torch.empty((300, 256), device="cuda")
 
@@ -106,7 +106,7 @@ def test_graph_replays_match_eager(torch):
     x1.copy_(to_dev(wl.random_x(1, k, 36)))
     x100.copy_(to_dev(wl.random_x(100, k, 37)))
     xb.copy_(to_dev(wl.random_x(70, 384, 38)))
-    b2[5].copy_(to_dev(wl.random_x(300, 2048, 40)))
+    b2[5].copy_(to_dev(wl.random_x(300, 4096, 40)))
     torch.cuda.synchronize()
     got = replay()
     want2 = eager()

@@ -99,7 +99,7 @@ def test_pool_grows_once_for_a_larger_call_and_per_stream(torch):
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("m,d_in,d_out,r", [(70, 384, 256, 128), (300, 2048, 256, 512)])
+@pytest.mark.parametrize("m,d_in,d_out,r", [(70, 384, 256, 128), (300, 4096, 256, 512)])
 def test_library_and_caller_workspaces_give_the_same_bits(torch, m, d_in, d_out, r):
     # the second size splits the first product's contraction over workgroups
     d = wl.blr_inputs(m=m, d_in=d_in, d_out=d_out, r=r, index=62)
