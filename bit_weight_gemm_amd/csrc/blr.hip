@@ -55,18 +55,15 @@ static bool half_buf(const GemmArgs &p) { return ((int64_t)p.M + 256) * p.lda * 
 
 // Products with the long contraction (GEMM1 over d_in, and the backward's db over
 // d_out), of M x r outputs, B a bitmap whose bits run along the outputs:
-// 32 x 64 tiles when they are few, else 128 x 128 tiles.  With an f16 A operand
-// each wave takes two 64-wide slices of a 512-wide step when the padded
-// contraction allows (fewer steps and barriers); with A staged from f32 x (x.g
-// rounded in the kernel) 256-wide steps with two A register stages are faster
-// (GEMM1 at M=512, d_in=4096, r=1024: 16.2 against 19.1 us alone, about 1 us
-// less per layer call).
+// 32 x 64 tiles when they are few, else 128 x 128 tiles.  256-wide steps with two
+// A register stages, for A staged from f32 x (x.g rounded in the kernel: GEMM1 at
+// M=512, d_in=4096, r=1024 16.2 against 19.1 us alone with 512-wide steps and one
+// stage) and for an f16 A alike (db at the same shape: 12.9 against 13.9 us).
 template <int EPI, int AMODE>
-static hipError_t gemm_long_k(const GemmArgs &p, int64_t kpad, bool small, hipStream_t s) {
+static hipError_t gemm_long_k(const GemmArgs &p, bool small, hipStream_t s) {
     constexpr bool half_a = AMODE == kAHalf || AMODE == kAHalfBuf;
     // (f32 pieces of x take twice the registers of f16 ones: two A register stages)
     if (!small) return run_gemm<128, 128, 1, 4, 1, 4, AMODE, false, EPI, 4, half_a ? 4 : 2, 1, kBSignT>(p, s);
-    if (half_a && kpad % 1024 == 0) return run_gemm<32, 64, 1, 2, 4, 2, AMODE, false, EPI, 2, 1, 2, kBSignT>(p, s);
     return run_gemm<32, 64, 1, 2, 4, 2, AMODE, false, EPI, 2, 2, 1, kBSignT>(p, s);
 }
 // Products with the short contraction r (GEMM2, and the backward's c and dx'), B
@@ -119,7 +116,7 @@ static bool xg_vector(const BlrPlan &pl, const float *x, const float *g) {
 template <int EPI>
 static hipError_t run_gemm1(const GemmArgs &p, const BlrPlan &pl, bool vec, hipStream_t s) {
     const bool small = blr_small_tiles(pl.M, pl.kpad2);
-    return vec ? gemm_long_k<EPI, kAXG>(p, pl.kpad1, small, s) : gemm_long_k<EPI, kAXGS>(p, pl.kpad1, small, s);
+    return vec ? gemm_long_k<EPI, kAXG>(p, small, s) : gemm_long_k<EPI, kAXGS>(p, small, s);
 }
 
 namespace {
@@ -434,8 +431,7 @@ static hipError_t backward_tail(const BlrBwdPlan &pb, const uint32_t *bits_u, co
         p.M = (int)M, p.N = (int)pl.kpad2, p.K = (int)pb.kpado, p.Kloop = (int)pb.kpado;
         p.alpha = 1.0f / gs, p.nrowf = (int)r, p.rowf = l;
         p.ea = a, p.ldea = r, p.part = part_dl, p.Ch = dbl, p.ldch = pl.kpad2, p.gs = gs;
-        e = half_buf(p) ? gemm_long_k<kEpiBwdDb, kAHalfBuf>(p, pb.kpado, small, s)
-                        : gemm_long_k<kEpiBwdDb, kAHalf>(p, pb.kpado, small, s);
+        e = half_buf(p) ? gemm_long_k<kEpiBwdDb, kAHalfBuf>(p, small, s) : gemm_long_k<kEpiBwdDb, kAHalf>(p, small, s);
         if (e != hipSuccess) return e;
     }
     // dx' = dbl . S_V^T / gs (not stored; contraction over r, along the rows of bits_v):
