@@ -48,7 +48,9 @@ def _bits_equal(a, b):
     return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
 
 
-SHAPES = [(1, 64, 64, 32, 1), (70, 45, 130, 96, 2), (129, 256, 77, 160, 3), (512, 4096, 4096, 1024, 1)]
+# the last two: the first product's contraction split over workgroups (two chunks, two paths), and not
+SHAPES = [(1, 64, 64, 32, 1), (70, 45, 130, 96, 2), (129, 256, 77, 160, 3), (300, 4096, 200, 1024, 2),
+          (512, 4096, 4096, 1024, 1)]
 
 
 @pytest.mark.parametrize("m,d_in,d_out,r,npaths", SHAPES)
