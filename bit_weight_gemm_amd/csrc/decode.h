@@ -63,6 +63,9 @@ __device__ __forceinline__ void word_m1(uint32_t w, uint32_t magic, h2 out[8]) {
 // in vector registers): v_bfi_b32 takes the mask from an SGPR and the word and
 // the 0x6400 pattern from VGPRs, and v_pk_fma_f16 takes the factor 4^-P and the
 // offset -(2^(10-2P) + 1) from the low and high halves of one SGPR (op_sel).
+// Written as inline asm, so only for vector-ALU consumers: the compiler does not
+// see these register writes when it spaces MFMA operand reads and writes, so
+// MFMA operands come from word_m1 / half_group_m1.
 constexpr uint32_t f16_bits(float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); }
 template <int P>
 __device__ __forceinline__ h2 pair_m1_s(uint32_t w, uint32_t magic) {

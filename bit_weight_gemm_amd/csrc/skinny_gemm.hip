@@ -4,12 +4,15 @@
 //
 // For M <= 16 (M*K <= 65536) the whole of x fits in LDS as f16, so a workgroup stages it once
 // and its waves then run without barriers: each wave streams the code words of
-// the workgroup's 32 output columns over its own share of K (a half, quarter or
-// eighth) straight from HBM into registers, several steps ahead, decodes them and issues
-// v_mfma_f32_32x32x16_f16 with A fragments read from LDS.  At the end the waves'
-// partial tiles are added through LDS in wave order, so the result does not
-// depend on timing.  Workgroups are N/32, so every CU takes part even when N is
-// a few thousand.
+// the workgroup's output columns over its own eighth of K straight from HBM into
+// registers, several steps ahead, decodes them and issues MFMAs with A fragments
+// read from LDS.  At the end the waves' partial tiles are added through LDS in
+// wave order, so the result does not depend on timing.  Two kernels:
+// skinny16_kernel (K a multiple of 1024) on v_mfma_f32_16x16x32_f16, each lane
+// owning one, two or four adjacent output columns, whose words of one group it
+// loads at once, with the block scale applied to each block's sum; and
+// skinny_kernel (other K) on v_mfma_f32_32x32x16_f16 with 32- or 64-column
+// workgroups and d folded into the f16 operand.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -51,25 +54,27 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
     const int nsteps = kw_wave / 64;   // a multiple of D
     const int kbeg = wave * kw_wave;
     int col[NBW];
-    uint32_t cbase[NBW], sbase[NBW];  // word offsets of (col, group kbeg/16) and (col, block kbeg/128)
+    uint32_t cbase[NBW], sbase[NBW];  // word offsets of (col, group kbeg/16) and (col, block 0)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
         col[nb] = n0 + 32 * nb + lrow;  // < Npad: padded rows are code 1
         cbase[nb] = (uint32_t)code_index(col[nb], kbeg >> 4, p.kw);
-        sbase[nb] = (uint32_t)scale_index(col[nb], kbeg / kBlock, p.kb);
+        sbase[nb] = (uint32_t)scale_index(col[nb], 0, p.kb);
     }
     uint32_t bw[D][NBW][4];
     uint16_t dv[D][NBW];
     // step t: groups kbeg/16 + 4t .. +3 (16 words apart per step, 4 per group),
-    // block kbeg/128 + t/2 (4 scales apart per block)
+    // block (kbeg + 64t)/128 (4 scales apart per block; with K % 1024 == 512 a
+    // wave's range starts half way through a block)
     auto load = [&](int slot, int t) {
         const uint32_t tc = (uint32_t)(t < nsteps ? t : nsteps - 1);  // clamped past the end
+        const uint32_t blk = ((uint32_t)(kbeg >> 6) + tc) >> 1;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
             const uint32_t *cw = p.codes + cbase[nb] + 16 * tc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) bw[slot][nb][i] = cw[4 * i];
-            dv[slot][nb] = p.scales[sbase[nb] + 4 * (tc >> 1)];
+            dv[slot][nb] = p.scales[sbase[nb] + 4 * blk];
         }
     };
     // ---- stage x once: f32 -> f16 (round to nearest even), 4 values per piece.
@@ -184,6 +189,169 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
     }
 }
 
+// ---- the same product on v_mfma_f32_16x16x32_f16 (no rows wasted at M <= 16),
+// for K a multiple of 1024 (eight waves, each owning whole 128-wide blocks).
+//
+// Lane l = 16q + c holds MFMA row/column slot c and k octet q.  It owns the CPL
+// adjacent weight rows (output columns) n0 + CPL*c + j, j < CPL: their code
+// words of one 16-wide group lie side by side in the device layout, so one
+// 4*CPL-byte load brings the lane all its words of a group, and one 2*CPL-byte
+// load its scales of a block.  In step t (64 k of the wave's slice) the lane
+// takes group 4t + q: elements 0..7 feed the step's first MFMA (MFMA k = 8q + i)
+// and elements 8..15 its second, and the A fragments read x at the same k, so
+// every decoded word feeds two MFMAs.  Column block j's MFMAs give the output
+// columns n0 + CPL*c + j.  The operands are the exact codes q - 1; each block's
+// two steps (four MFMAs per column block) accumulate from zero, and the block's
+// sum is then scaled by d in f32 and added to the lane's total, so the decode
+// has no per-weight scaling.  At the end the waves' totals are added in wave
+// order through LDS, as in skinny_kernel.
+template <int CPL, int D, int U>
+__global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
+    constexpr int WK = 8;
+    constexpr int SW = (CPL + 1) / 2;  // 32-bit words holding the lane's CPL scales
+    typedef uint32_t uw __attribute__((ext_vector_type(CPL)));
+    typedef uint32_t us __attribute__((ext_vector_type(SW)));
+    typedef uint16_t us1;
+    typedef float fv __attribute__((ext_vector_type(CPL)));
+    extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = lane & 15, q = lane >> 4;
+    const int nl = blockIdx.x * (16 * CPL) + CPL * c;  // the lane's first column (< Npad)
+    const uint32_t magic = f16_magic();
+
+    // ---- this wave's K range; the lane's words of group kbeg/16 + q and scales
+    // of block kbeg/128 (each step moves 4 groups = 64 bytes of words, each block
+    // 4 scales = 8 bytes)
+    const int kw_wave = p.K / WK;     // a multiple of 128
+    const int nsteps = kw_wave / 64;  // even, a multiple of D
+    const int kbeg = wave * kw_wave;
+    const char *cp = reinterpret_cast<const char *>(p.codes) + code_index(nl, (kbeg >> 4) + q, p.kw) * 4;
+    const char *sp = reinterpret_cast<const char *>(p.scales) + scale_index(nl, kbeg / kBlock, p.kb) * 2;
+    uw bw[D];
+    uint32_t dv[D][SW];
+    auto load = [&](int slot, int t) {
+        const uint32_t tc = (uint32_t)(t < nsteps ? t : nsteps - 1);  // clamped past the end
+        bw[slot] = *reinterpret_cast<const uw *>(cp + tc * 64u);
+        if constexpr (CPL == 1) {
+            dv[slot][0] = *reinterpret_cast<const us1 *>(sp + (tc >> 1) * 8u);
+        } else {
+            const us v = *reinterpret_cast<const us *>(sp + (tc >> 1) * 8u);
+#pragma unroll
+            for (int i = 0; i < SW; ++i) dv[slot][i] = v[i];
+        }
+    };
+    // ---- stage the wave's slice of x as f16, as skinny_kernel does
+    const int qw = kw_wave / 4;
+    const int total = p.M * qw;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    f4 xv[U];
+    const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
+    const int s0 = (lane + start) % total;
+    const int r0 = s0 / qw, q0 = s0 % qw;
+    const int adv_r = (64 / qw) % p.M, adv_q = 64 % qw;
+    auto next = [&](int &r, int &k4) {
+        k4 += adv_q;
+        r += adv_r;
+        if (k4 >= qw) {
+            k4 -= qw;
+            ++r;
+        }
+        if (r >= p.M) r -= p.M;
+    };
+    {
+        int r = r0, k4 = q0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = u * 64 + lane < total;
+            xv[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + kbeg + 4 * (live ? k4 : q0));
+            next(r, k4);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        int r = r0, k4 = q0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u * 64 + lane < total) {
+                const h4 h = {(_Float16)xv[u][0], (_Float16)xv[u][1], (_Float16)xv[u][2], (_Float16)xv[u][3]};
+                *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 4 * k4]) = h;
+            }
+            next(r, k4);
+        }
+    }
+
+    f4 acc[CPL], blk[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) acc[j] = f4{}, blk[j] = f4{};
+    const int arow = c < p.M ? c : p.M - 1;  // rows past M repeat row M-1; never stored
+    const _Float16 *xrow = xs + xs_row(arow, p.K) + kbeg + 16 * q;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int t0 = 0; t0 < nsteps; t0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const _Float16 *xa = xrow + (t0 + s) * 64;
+            const h8 a0 = *reinterpret_cast<const h8 *>(xa), a1 = *reinterpret_cast<const h8 *>(xa + 8);
+            h8 b1[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                h2 pr[8];
+                word_m1(bw[s][j], magic, pr);
+                const h8 b0 = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
+                b1[j] = h8{pr[4].x, pr[4].y, pr[5].x, pr[5].y, pr[6].x, pr[6].y, pr[7].x, pr[7].y};
+                // a block's first step starts its sums from zero
+                blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, (s & 1) ? blk[j] : f4{}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], blk[j], 0, 0, 0);
+            if (s & 1) {  // the block's second step: add d * (block sum) to the total
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    // column j's scale: half j % 2 of word j / 2, taken with a shift
+                    const uint32_t dw = dv[s][j >> 1];
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? dw >> 16 : dw & 0xFFFFu));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(d, blk[j][i], acc[j][i]);
+                }
+            }
+            load(s, t0 + s + D);
+        }
+    }
+
+    // ---- the waves' totals added in wave order.  Register i of column block j
+    // holds row 4q + i of column nl + j; every wave leaves its four rows' values in
+    // LDS (the lane's CPL columns side by side), then waves 0..3 each add one
+    // register's over the waves and store the row's CPL columns.
+    __syncthreads();
+    fv *red = reinterpret_cast<fv *>(xs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fv v;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) v[j] = acc[j][i];
+        red[(wave * 4 + i) * 64 + lane] = v;
+    }
+    __syncthreads();
+    if (wave < 4) {
+        const int i = wave, row = 4 * q + i;
+        fv v = red[i * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) v += red[(w * 4 + i) * 64 + lane];
+        if (row < p.M) {
+            float *yr = p.y + (int64_t)row * p.N;
+            if (p.N % CPL == 0 && nl + CPL <= p.N) {
+                *reinterpret_cast<fv *>(yr + nl) = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j)
+                    if (nl + j < p.N) yr[nl + j] = v[j];
+            }
+        }
+    }
+}
+
 template <int NBW, int WK, int D, int U>
 hipError_t run_skinny(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
     // raise the kernel's dynamic LDS limit once per device (bit dev of the mask)
@@ -209,10 +377,12 @@ bool skinny_fits(const DevWeight &w, int64_t M) {
     if (M < 1 || M > kSkinnyMaxM || w.K % 512 != 0 || M * w.K > 4 * 512 * 32 ||
         (size_t)M * (w.K + 8) * 2 > kSkinnyMaxLds)
         return false;
-    // More than 16 pieces per thread only with 32-column workgroups (N <= 8192):
-    // measured with cold weights at K = 4096, M = 12..16, the skinny kernel takes
-    // 10.1-10.3 us against the tiled kernel's 13.1 at N = 4096, but 14.3 against
-    // 13.7-13.8 at N = 14336 (64-column workgroups, each staging all of x).
+    // skinny16_kernel (K % 1024 == 0) at any N: measured with cold weights at
+    // K = 4096, N = 14336, M = 9..16 take 10.9-11.7 us against the tiled kernel's
+    // 13.4.  skinny_kernel: more than 16 pieces per thread only with 32-column
+    // workgroups (N <= 8192), where M = 12..16 took 10.1-10.3 us against 13.1 at
+    // N = 4096, but 14.3 against 13.7-13.8 at N = 14336.
+    if (w.K % 1024 == 0) return true;
     return M * w.K <= 4 * 512 * 16 || (w.N + 31) / 32 <= 256;
 }
 
@@ -228,6 +398,52 @@ hipError_t run_skinny_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s)
     return run_skinny<NBW, 8, D, 16>(a, lds, dev, s);
 }
 
+template <int CPL, int D, int U>
+hipError_t run_skinny16(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+    static std::atomic<uint64_t> attr_set{0};
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!bit || !(attr_set.load() & bit)) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, U>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(bit);
+    }
+    const unsigned blocks = (unsigned)((a.N + 16 * CPL - 1) / (16 * CPL));
+    skinny16_kernel<CPL, D, U><<<dim3(blocks), dim3(512), lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int CPL, int D>
+hipError_t run_skinny16_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+    const int64_t per_thread = ((int64_t)a.M * a.K / 4 + 511) / 512;
+    if (per_thread <= 2) return run_skinny16<CPL, D, 2>(a, lds, dev, s);
+    if (per_thread <= 16) return run_skinny16<CPL, D, 16>(a, lds, dev, s);
+    return run_skinny16<CPL, D, 32>(a, lds, dev, s);
+}
+
+template <int CPL>
+hipError_t run_skinny16_d(const SkinnyArgs &a, int dev, hipStream_t s) {
+    // LDS: x as f16 (padded rows), later the eight waves' four rows of CPL columns
+    const size_t xb = (size_t)a.M * (a.K + 8) * 2, rb = (size_t)8 * 4 * 64 * CPL * 4;
+    const size_t lds = xb > rb ? xb : rb;
+    const int steps = a.K / 512;  // per wave: even
+    if (steps % 8 == 0) return run_skinny16_u<CPL, 8>(a, lds, dev, s);
+    if (steps % 4 == 0) return run_skinny16_u<CPL, 4>(a, lds, dev, s);
+    return run_skinny16_u<CPL, 2>(a, lds, dev, s);
+}
+
+// Columns per lane of skinny16_kernel: the widest that still gives about three
+// workgroups for every four CUs (each workgroup stages all of x, so more
+// workgroups than that only add x traffic).  Measured with cold weights at
+// K = 4096: M = 8, N = 14336 takes 10.3 us with four columns per lane (224
+// workgroups), 12.8 with two, 13.9 with one; M = 1, N = 4096 takes 4.1 us with
+// one (256 workgroups), 6.0 with two and 8.3 with four.
+static int skinny16_columns(int64_t N) {
+    for (int cpl = 4; cpl > 1; cpl /= 2)
+        if ((N + 16 * cpl - 1) / (16 * cpl) >= 192) return cpl;
+    return 1;
+}
+
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s) {
     SkinnyArgs a{};
     a.x = x;
@@ -239,6 +455,12 @@ hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M
     a.K = (int)w.K;
     a.kw = (int)(w.K / 16);
     a.kb = (int)(w.K / kBlock);
+    if (w.K % 1024 == 0) {
+        const int cpl = skinny16_columns(w.N);
+        if (cpl == 4) return run_skinny16_d<4>(a, dev, s);
+        if (cpl == 2) return run_skinny16_d<2>(a, dev, s);
+        return run_skinny16_d<1>(a, dev, s);
+    }
     // Eight waves; wave w owns K/8, i.e. K/512 steps, in a multiple of the
     // prefetch depth D.  LDS: x as f16 (padded rows), later the waves' sums.
     const size_t xb = (size_t)M * (w.K + 8) * 2, rb = (size_t)8 * 16 * 64 * 4;

@@ -38,8 +38,10 @@ CASES = [
     ("gemv_mt M=2..4", "f32", (2, 3, 4), 1000, 1024),
     ("gemv_f32 eight rows per lane, M=2", "f32", (2,), 5000, 1024),
     ("gemv_f32 eight rows per lane, M=3 and forced M=7", "f32", (3, 7), 5000, 1024),
-    ("skinny, 32-column workgroups (M=16: 32 pieces of x per thread)", "mfma", (1, 8, 16), 1000, 4096),
-    ("skinny, 64-column workgroups", "mfma", (4,), 9000, 2048),
+    ("skinny 16x16x32, one column per lane (M=16: 32 pieces of x per thread)", "mfma", (1, 8, 16), 1000, 4096),
+    ("skinny 16x16x32, two columns per lane", "mfma", (4,), 9000, 2048),
+    ("skinny 16x16x32, four columns per lane, N % 4 == 2", "mfma", (2, 12), 12302, 1024),
+    ("skinny 32x32x16, K not a multiple of 1024", "mfma", (4, 12), 1000, 1536),
     ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
     ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
