@@ -10,12 +10,14 @@
 // wave order, so the result does not depend on timing.  Two kernels:
 // skinny16_kernel (K a multiple of 1024) on v_mfma_f32_16x16x32_f16, each lane
 // owning one, two or four adjacent output columns, whose words of one group it
-// loads at once, with the block scale applied to each block's sum; and
+// loads at once, with the block scale applied to each block's sum and x staged
+// into LDS step by step or all at once; and
 // skinny_kernel (other K) on v_mfma_f32_32x32x16_f16 with 32- or 64-column
 // workgroups and d folded into the f16 operand.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "decode.h"
 #include "internal.h"
@@ -203,16 +205,32 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
 // columns n0 + CPL*c + j.  The operands are the exact codes q - 1; each block's
 // two steps (four MFMAs per column block) accumulate from zero, and the block's
 // sum is then scaled by d in f32 and added to the lane's total, so the decode
-// has no per-weight scaling.  At the end the waves' totals are added in wave
-// order through LDS, as in skinny_kernel.
-template <int CPL, int D, int U>
+// has no per-weight scaling.
+//
+// x is staged in one of two ways (XM).  Step by step (XM = PPS > 0): a load
+// slot holds one step's x pieces (rows 4i + q, i < PPS, k 4c .. 4c+3 of the
+// step, f32), code words and scales, and the slots of D steps are in flight;
+// the loads go out step by step, x with its step's words, so a step waits only
+// for its own data (the memory counter retires in issue order), and each
+// step's x is rounded to f16 into LDS after the MFMAs of the step before.  All
+// at once (XM = -U < 0): the wave's whole slice of x is loaded first (U pieces
+// per lane, each workgroup starting at its own offset), then the code words
+// of D steps, and x is in LDS before the first step.  Either way the wave reads
+// only the x it stores itself, so no barrier is needed, and the last D steps
+// issue no further loads.  At the end the waves' totals are added in wave order
+// through LDS, as in skinny_kernel.
+template <int CPL, int D, int XM>
 __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     constexpr int WK = 8;
-    constexpr int SW = (CPL + 1) / 2;  // 32-bit words holding the lane's CPL scales
+    constexpr bool PROG = XM > 0;
+    constexpr int PPS = PROG ? XM : 1;  // x pieces per lane and step (step by step)
+    constexpr int U = PROG ? 1 : -XM;   // x pieces per lane (all at once)
+    constexpr int SW = (CPL + 1) / 2;   // 32-bit words holding the lane's CPL scales
     typedef uint32_t uw __attribute__((ext_vector_type(CPL)));
     typedef uint32_t us __attribute__((ext_vector_type(SW)));
     typedef uint16_t us1;
     typedef float fv __attribute__((ext_vector_type(CPL)));
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int c = lane & 15, q = lane >> 4;
@@ -227,59 +245,93 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     const int kbeg = wave * kw_wave;
     const char *cp = reinterpret_cast<const char *>(p.codes) + code_index(nl, (kbeg >> 4) + q, p.kw) * 4;
     const char *sp = reinterpret_cast<const char *>(p.scales) + scale_index(nl, kbeg / kBlock, p.kb) * 2;
+    const float *xg[PPS];  // step by step: rows past M re-read row M-1 (never stored)
+#pragma unroll
+    for (int i = 0; i < PPS; ++i) {
+        const int r = 4 * i + q;
+        xg[i] = p.x + (int64_t)(r < p.M ? r : p.M - 1) * p.K + kbeg + 4 * c;
+    }
     uw bw[D];
     uint32_t dv[D][SW];
+    f4 xv[D][PPS];
     auto load = [&](int slot, int t) {
-        const uint32_t tc = (uint32_t)(t < nsteps ? t : nsteps - 1);  // clamped past the end
-        bw[slot] = *reinterpret_cast<const uw *>(cp + tc * 64u);
-        if constexpr (CPL == 1) {
-            dv[slot][0] = *reinterpret_cast<const us1 *>(sp + (tc >> 1) * 8u);
-        } else {
-            const us v = *reinterpret_cast<const us *>(sp + (tc >> 1) * 8u);
+        if constexpr (PROG) {
 #pragma unroll
-            for (int i = 0; i < SW; ++i) dv[slot][i] = v[i];
+            for (int i = 0; i < PPS; ++i) xv[slot][i] = *reinterpret_cast<const f4 *>(xg[i] + 64 * t);
         }
-    };
-    // ---- stage the wave's slice of x as f16, as skinny_kernel does
-    const int qw = kw_wave / 4;
-    const int total = p.M * qw;
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    f4 xv[U];
-    const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
-    const int s0 = (lane + start) % total;
-    const int r0 = s0 / qw, q0 = s0 % qw;
-    const int adv_r = (64 / qw) % p.M, adv_q = 64 % qw;
-    auto next = [&](int &r, int &k4) {
-        k4 += adv_q;
-        r += adv_r;
-        if (k4 >= qw) {
-            k4 -= qw;
-            ++r;
-        }
-        if (r >= p.M) r -= p.M;
-    };
-    {
-        int r = r0, k4 = q0;
+        bw[slot] = *reinterpret_cast<const uw *>(cp + (uint32_t)t * 64u);
+        if (slot & 1) {  // a block's scales, with its second step
+            const char *sb = sp + (uint32_t)(t >> 1) * 8u;
+            if constexpr (CPL == 1) {
+                dv[slot][0] = *reinterpret_cast<const us1 *>(sb);
+            } else {
+                const us v = *reinterpret_cast<const us *>(sb);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool live = u * 64 + lane < total;
-            xv[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + kbeg + 4 * (live ? k4 : q0));
-            next(r, k4);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    __builtin_amdgcn_sched_barrier(0);
-    {
-        int r = r0, k4 = q0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u * 64 + lane < total) {
-                const h4 h = {(_Float16)xv[u][0], (_Float16)xv[u][1], (_Float16)xv[u][2], (_Float16)xv[u][3]};
-                *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 4 * k4]) = h;
+                for (int i = 0; i < SW; ++i) dv[slot][i] = v[i];
             }
-            next(r, k4);
+        }
+    };
+    auto stage = [&](int slot, int t) {  // step t's x, rounded to f16 (nearest even), into LDS
+        if constexpr (PROG) {
+#pragma unroll
+            for (int i = 0; i < PPS; ++i) {
+                const int r = 4 * i + q;
+                if (r < p.M) {
+                    const h4 h = {(_Float16)xv[slot][i][0], (_Float16)xv[slot][i][1], (_Float16)xv[slot][i][2],
+                                  (_Float16)xv[slot][i][3]};
+                    *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 64 * t + 4 * c]) = h;
+                }
+            }
+        }
+    };
+
+    if constexpr (PROG) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) load(s, s);
+        stage(0, 0);
+    } else {
+        // the wave's slice of x, M*qw pieces of 4 values: lane l takes pieces
+        // (start + l + 64u) mod M*qw, tracked as (row, piece in row)
+        const int qw = kw_wave / 4;
+        const int total = p.M * qw;
+        f4 xa[U];
+        const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
+        const int s0 = (lane + start) % total;
+        const int r0 = s0 / qw, q0 = s0 % qw;
+        const int adv_r = (64 / qw) % p.M, adv_q = 64 % qw;
+        auto next = [&](int &r, int &k4) {
+            k4 += adv_q;
+            r += adv_r;
+            if (k4 >= qw) {
+                k4 -= qw;
+                ++r;
+            }
+            if (r >= p.M) r -= p.M;
+        };
+        {
+            int r = r0, k4 = q0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool live = u * 64 + lane < total;
+                xa[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + kbeg +
+                                                      4 * (live ? k4 : q0));
+                next(r, k4);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code-word loads
+#pragma unroll
+        for (int s = 0; s < D; ++s) load(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            int r = r0, k4 = q0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u * 64 + lane < total) {
+                    const h4 h = {(_Float16)xa[u][0], (_Float16)xa[u][1], (_Float16)xa[u][2], (_Float16)xa[u][3]};
+                    *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 4 * k4]) = h;
+                }
+                next(r, k4);
+            }
         }
     }
 
@@ -288,37 +340,48 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     for (int j = 0; j < CPL; ++j) acc[j] = f4{}, blk[j] = f4{};
     const int arow = c < p.M ? c : p.M - 1;  // rows past M repeat row M-1; never stored
     const _Float16 *xrow = xs + xs_row(arow, p.K) + kbeg + 16 * q;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int t0 = 0; t0 < nsteps; t0 += D) {
+    // step t from slot s: the MFMAs, then (step by step) the next step's x into
+    // LDS, then (MORE) the loads of step t + D into the slot
+    auto body = [&](auto more, int s, int t) {
+        const _Float16 *xa = xrow + t * 64;
+        const h8 a0 = *reinterpret_cast<const h8 *>(xa), a1 = *reinterpret_cast<const h8 *>(xa + 8);
+        h8 b1[CPL];
 #pragma unroll
-        for (int s = 0; s < D; ++s) {
-            const _Float16 *xa = xrow + (t0 + s) * 64;
-            const h8 a0 = *reinterpret_cast<const h8 *>(xa), a1 = *reinterpret_cast<const h8 *>(xa + 8);
-            h8 b1[CPL];
+        for (int j = 0; j < CPL; ++j) {
+            h2 pr[8];
+            word_m1(bw[s][j], magic, pr);
+            const h8 b0 = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
+            b1[j] = h8{pr[4].x, pr[4].y, pr[5].x, pr[5].y, pr[6].x, pr[6].y, pr[7].x, pr[7].y};
+            // a block's first step starts its sums from zero
+            blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, (s & 1) ? blk[j] : f4{}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], blk[j], 0, 0, 0);
+        if (s & 1) {  // the block's second step: add d * (block sum) to the total
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                h2 pr[8];
-                word_m1(bw[s][j], magic, pr);
-                const h8 b0 = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
-                b1[j] = h8{pr[4].x, pr[4].y, pr[5].x, pr[5].y, pr[6].x, pr[6].y, pr[7].x, pr[7].y};
-                // a block's first step starts its sums from zero
-                blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, (s & 1) ? blk[j] : f4{}, 0, 0, 0);
+                // column j's scale: half j % 2 of word j / 2, taken with a shift
+                const uint32_t dw = dv[s][j >> 1];
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? dw >> 16 : dw & 0xFFFFu));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(d, blk[j][i], acc[j][i]);
             }
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], blk[j], 0, 0, 0);
-            if (s & 1) {  // the block's second step: add d * (block sum) to the total
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    // column j's scale: half j % 2 of word j / 2, taken with a shift
-                    const uint32_t dw = dv[s][j >> 1];
-                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? dw >> 16 : dw & 0xFFFFu));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(d, blk[j][i], acc[j][i]);
-                }
-            }
-            load(s, t0 + s + D);
         }
+        if (s + 1 < D)
+            stage(s + 1, t + 1);
+        else if (decltype(more)::value)
+            stage(0, t + 1);
+        if constexpr (decltype(more)::value) load(s, t + D);
+    };
+    // the wave's own x is in LDS once its stores are done (no barrier)
+    if constexpr (!PROG) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    int t0 = 0;
+    for (; t0 + D < nsteps; t0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) body(std::true_type{}, s, t0 + s);
     }
+#pragma unroll
+    for (int s = 0; s < D; ++s) body(std::false_type{}, s, t0 + s);
 
     // ---- the waves' totals added in wave order.  Register i of column block j
     // holds row 4q + i of column nl + j; every wave leaves its four rows' values in
@@ -398,27 +461,46 @@ hipError_t run_skinny_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s)
     return run_skinny<NBW, 8, D, 16>(a, lds, dev, s);
 }
 
-template <int CPL, int D, int U>
+template <int CPL, int D, int XM>
 hipError_t run_skinny16(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
     static std::atomic<uint64_t> attr_set{0};
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!bit || !(attr_set.load() & bit)) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, U>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, XM>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyMaxLds);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit);
     }
     const unsigned blocks = (unsigned)((a.N + 16 * CPL - 1) / (16 * CPL));
-    skinny16_kernel<CPL, D, U><<<dim3(blocks), dim3(512), lds, s>>>(a);
+    skinny16_kernel<CPL, D, XM><<<dim3(blocks), dim3(512), lds, s>>>(a);
     return hipGetLastError();
 }
 
+// How x is staged, measured with cold weights at K = 4096 (us per call, all at
+// once / step by step): with four columns per lane step by step wins at every M
+// (N = 14336: M = 1 9.15 / 8.05, M = 8 9.88 / 9.09, M = 16 11.6 / 10.6); with
+// one or two only for 2 <= M <= 4 (N = 4096, M = 2: 5.01 / 4.60; N = 8192,
+// M = 4: 7.12 / 6.27), and all at once for M = 1 (4.15 / 4.60) and M > 4
+// (N = 8192, M = 16: 8.95 / 9.86).  Step by step takes ceil(M/4) pieces per lane
+// and step (three take four); all at once the fewest of 2, 16 or 32 per lane
+// that cover the wave's slice.
 template <int CPL, int D>
-hipError_t run_skinny16_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
-    const int64_t per_thread = ((int64_t)a.M * a.K / 4 + 511) / 512;
-    if (per_thread <= 2) return run_skinny16<CPL, D, 2>(a, lds, dev, s);
-    if (per_thread <= 16) return run_skinny16<CPL, D, 16>(a, lds, dev, s);
-    return run_skinny16<CPL, D, 32>(a, lds, dev, s);
+hipError_t run_skinny16_x(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+    if (CPL == 4 || (a.M >= 2 && a.M <= 4)) {
+        if (a.M <= 4) return run_skinny16<CPL, D, 1>(a, lds, dev, s);
+        if constexpr (CPL == 4) {
+            if (a.M <= 8) return run_skinny16<CPL, D, 2>(a, lds, dev, s);
+            // four pieces per lane keep four steps in flight (eight spill)
+            return run_skinny16<CPL, D == 8 ? 4 : D, 4>(a, lds, dev, s);
+        }
+    }
+    if constexpr (CPL != 4) {
+        const int64_t per_thread = ((int64_t)a.M * a.K / 4 + 511) / 512;
+        if (per_thread <= 2) return run_skinny16<CPL, D, -2>(a, lds, dev, s);
+        if (per_thread <= 16) return run_skinny16<CPL, D, -16>(a, lds, dev, s);
+        return run_skinny16<CPL, D, -32>(a, lds, dev, s);
+    }
+    return hipErrorInvalidValue;  // not reached: four columns per lane always go step by step
 }
 
 template <int CPL>
@@ -427,9 +509,9 @@ hipError_t run_skinny16_d(const SkinnyArgs &a, int dev, hipStream_t s) {
     const size_t xb = (size_t)a.M * (a.K + 8) * 2, rb = (size_t)8 * 4 * 64 * CPL * 4;
     const size_t lds = xb > rb ? xb : rb;
     const int steps = a.K / 512;  // per wave: even
-    if (steps % 8 == 0) return run_skinny16_u<CPL, 8>(a, lds, dev, s);
-    if (steps % 4 == 0) return run_skinny16_u<CPL, 4>(a, lds, dev, s);
-    return run_skinny16_u<CPL, 2>(a, lds, dev, s);
+    if (steps % 8 == 0) return run_skinny16_x<CPL, 8>(a, lds, dev, s);
+    if (steps % 4 == 0) return run_skinny16_x<CPL, 4>(a, lds, dev, s);
+    return run_skinny16_x<CPL, 2>(a, lds, dev, s);
 }
 
 // Columns per lane of skinny16_kernel: the widest that still gives about three

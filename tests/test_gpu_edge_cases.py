@@ -38,9 +38,14 @@ CASES = [
     ("gemv_mt M=2..4", "f32", (2, 3, 4), 1000, 1024),
     ("gemv_f32 eight rows per lane, M=2", "f32", (2,), 5000, 1024),
     ("gemv_f32 eight rows per lane, M=3 and forced M=7", "f32", (3, 7), 5000, 1024),
-    ("skinny 16x16x32, one column per lane (M=16: 32 pieces of x per thread)", "mfma", (1, 8, 16), 1000, 4096),
-    ("skinny 16x16x32, two columns per lane", "mfma", (4,), 9000, 2048),
+    ("skinny 16x16x32, one column per lane, x all at once (M=16: 32 pieces per thread)", "mfma", (1, 8, 16),
+     1000, 4096),
+    ("skinny 16x16x32, one column per lane, two passes of eight steps (M=3 step by step)", "mfma", (1, 3, 5),
+     1000, 8192),
+    ("skinny 16x16x32, two columns per lane (M=3 step by step, M=12 all at once)", "mfma", (3, 12), 9000, 2048),
     ("skinny 16x16x32, four columns per lane, N % 4 == 2", "mfma", (2, 12), 12302, 1024),
+    ("skinny 16x16x32, four columns per lane, two and four pieces per step (M=13: two passes)", "mfma", (6, 13),
+     12302, 4096),
     ("skinny 32x32x16, K not a multiple of 1024", "mfma", (4, 12), 1000, 1536),
     ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
