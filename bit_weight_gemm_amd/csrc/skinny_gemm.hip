@@ -11,7 +11,7 @@
 // skinny16_kernel (K a multiple of 1024) on v_mfma_f32_16x16x32_f16, each lane
 // owning one, two or four adjacent output columns, whose words of one group it
 // loads at once, with the block scale applied to each block's sum and x staged
-// into LDS step by step or all at once; and
+// into LDS step by step; and
 // skinny_kernel (other K) on v_mfma_f32_32x32x16_f16 with 32- or 64-column
 // workgroups and d folded into the f16 operand.
 #include <hip/hip_runtime.h>
@@ -207,25 +207,18 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
 // sum is then scaled by d in f32 and added to the lane's total, so the decode
 // has no per-weight scaling.
 //
-// x is staged in one of two ways (XM).  Step by step (XM = PPS > 0): a load
-// slot holds one step's x pieces (rows 4i + q, i < PPS, k 4c .. 4c+3 of the
-// step, f32), code words and scales, and the slots of D steps are in flight;
-// the loads go out step by step, x with its step's words, so a step waits only
-// for its own data (the memory counter retires in issue order), and each
-// step's x is rounded to f16 into LDS after the MFMAs of the step before.  All
-// at once (XM = -U < 0): the wave's whole slice of x is loaded first (U pieces
-// per lane, each workgroup starting at its own offset), then the code words
-// of D steps, and x is in LDS before the first step.  Either way the wave reads
-// only the x it stores itself, so no barrier is needed, and the last D steps
-// issue no further loads.  At the end the waves' totals are added in wave order
-// through LDS, as in skinny_kernel.
-template <int CPL, int D, int XM>
+// x is staged step by step: a load slot holds one step's x pieces (rows 4i + q,
+// i < PPS, k 4c .. 4c+3 of the step, f32), code words and scales, and the slots
+// of D steps are in flight.  The loads go out step by step, x with its step's
+// words, so a step waits only for its own data (the memory counter retires in
+// issue order), and each step's x is rounded to f16 into LDS after the MFMAs of
+// the step before.  The wave reads only the x it stores itself, so no barrier
+// is needed, and the last D steps issue no further loads.  At the end the
+// waves' totals are added in wave order through LDS, as in skinny_kernel.
+template <int CPL, int D, int PPS>
 __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     constexpr int WK = 8;
-    constexpr bool PROG = XM > 0;
-    constexpr int PPS = PROG ? XM : 1;  // x pieces per lane and step (step by step)
-    constexpr int U = PROG ? 1 : -XM;   // x pieces per lane (all at once)
-    constexpr int SW = (CPL + 1) / 2;   // 32-bit words holding the lane's CPL scales
+    constexpr int SW = (CPL + 1) / 2;  // 32-bit words holding the lane's CPL scales
     typedef uint32_t uw __attribute__((ext_vector_type(CPL)));
     typedef uint32_t us __attribute__((ext_vector_type(SW)));
     typedef uint16_t us1;
@@ -245,7 +238,7 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     const int kbeg = wave * kw_wave;
     const char *cp = reinterpret_cast<const char *>(p.codes) + code_index(nl, (kbeg >> 4) + q, p.kw) * 4;
     const char *sp = reinterpret_cast<const char *>(p.scales) + scale_index(nl, kbeg / kBlock, p.kb) * 2;
-    const float *xg[PPS];  // step by step: rows past M re-read row M-1 (never stored)
+    const float *xg[PPS];  // rows past M re-read row M-1
 #pragma unroll
     for (int i = 0; i < PPS; ++i) {
         const int r = 4 * i + q;
@@ -255,10 +248,8 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     uint32_t dv[D][SW];
     f4 xv[D][PPS];
     auto load = [&](int slot, int t) {
-        if constexpr (PROG) {
 #pragma unroll
-            for (int i = 0; i < PPS; ++i) xv[slot][i] = *reinterpret_cast<const f4 *>(xg[i] + 64 * t);
-        }
+        for (int i = 0; i < PPS; ++i) xv[slot][i] = *reinterpret_cast<const f4 *>(xg[i] + 64 * t);
         bw[slot] = *reinterpret_cast<const uw *>(cp + (uint32_t)t * 64u);
         if (slot & 1) {  // a block's scales, with its second step
             const char *sb = sp + (uint32_t)(t >> 1) * 8u;
@@ -271,77 +262,40 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
             }
         }
     };
-    auto stage = [&](int slot, int t) {  // step t's x, rounded to f16 (nearest even), into LDS
-        if constexpr (PROG) {
+    // step t's x, rounded to f16 (nearest even), into LDS.  Rows past M hold
+    // row M-1's values and store them at row M-1 again (the same bits), so the
+    // stores need no branch: a branch would take the loads that feed them in,
+    // and its wait would then count every load in flight.
+    int xrow_s[PPS];
 #pragma unroll
-            for (int i = 0; i < PPS; ++i) {
-                const int r = 4 * i + q;
-                if (r < p.M) {
-                    const h4 h = {(_Float16)xv[slot][i][0], (_Float16)xv[slot][i][1], (_Float16)xv[slot][i][2],
-                                  (_Float16)xv[slot][i][3]};
-                    *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 64 * t + 4 * c]) = h;
-                }
-            }
+    for (int i = 0; i < PPS; ++i) {
+        const int r = 4 * i + q;
+        xrow_s[i] = xs_row(r < p.M ? r : p.M - 1, p.K) + kbeg + 4 * c;
+    }
+    auto stage = [&](int slot, int t) {
+#pragma unroll
+        for (int i = 0; i < PPS; ++i) {
+            const h4 h = {(_Float16)xv[slot][i][0], (_Float16)xv[slot][i][1], (_Float16)xv[slot][i][2],
+                          (_Float16)xv[slot][i][3]};
+            *reinterpret_cast<h4 *>(&xs[xrow_s[i] + 64 * t]) = h;
         }
     };
 
-    if constexpr (PROG) {
+    // the first D steps' loads in step order (kept so by the scheduling barriers)
 #pragma unroll
-        for (int s = 0; s < D; ++s) load(s, s);
-        stage(0, 0);
-    } else {
-        // the wave's slice of x, M*qw pieces of 4 values: lane l takes pieces
-        // (start + l + 64u) mod M*qw, tracked as (row, piece in row)
-        const int qw = kw_wave / 4;
-        const int total = p.M * qw;
-        f4 xa[U];
-        const int start = (int)(((unsigned)blockIdx.x * 2053u) % (unsigned)total);
-        const int s0 = (lane + start) % total;
-        const int r0 = s0 / qw, q0 = s0 % qw;
-        const int adv_r = (64 / qw) % p.M, adv_q = 64 % qw;
-        auto next = [&](int &r, int &k4) {
-            k4 += adv_q;
-            r += adv_r;
-            if (k4 >= qw) {
-                k4 -= qw;
-                ++r;
-            }
-            if (r >= p.M) r -= p.M;
-        };
-        {
-            int r = r0, k4 = q0;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool live = u * 64 + lane < total;
-                xa[u] = *reinterpret_cast<const f4 *>(p.x + (int64_t)(live ? r : r0) * p.K + kbeg +
-                                                      4 * (live ? k4 : q0));
-                next(r, k4);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code-word loads
-#pragma unroll
-        for (int s = 0; s < D; ++s) load(s, s);
+    for (int s = 0; s < D; ++s) {
+        load(s, s);
         __builtin_amdgcn_sched_barrier(0);
-        {
-            int r = r0, k4 = q0;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (u * 64 + lane < total) {
-                    const h4 h = {(_Float16)xa[u][0], (_Float16)xa[u][1], (_Float16)xa[u][2], (_Float16)xa[u][3]};
-                    *reinterpret_cast<h4 *>(&xs[xs_row(r, p.K) + kbeg + 4 * k4]) = h;
-                }
-                next(r, k4);
-            }
-        }
     }
+    stage(0, 0);
 
     f4 acc[CPL], blk[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[j] = f4{}, blk[j] = f4{};
     const int arow = c < p.M ? c : p.M - 1;  // rows past M repeat row M-1; never stored
     const _Float16 *xrow = xs + xs_row(arow, p.K) + kbeg + 16 * q;
-    // step t from slot s: the MFMAs, then (step by step) the next step's x into
-    // LDS, then (MORE) the loads of step t + D into the slot
+    // step t from slot s: the MFMAs, then the next step's x into LDS, then
+    // (MORE) the loads of step t + D into the slot
     auto body = [&](auto more, int s, int t) {
         const _Float16 *xa = xrow + t * 64;
         const h8 a0 = *reinterpret_cast<const h8 *>(xa), a1 = *reinterpret_cast<const h8 *>(xa + 8);
@@ -373,15 +327,21 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
             stage(0, t + 1);
         if constexpr (decltype(more)::value) load(s, t + D);
     };
-    // the wave's own x is in LDS once its stores are done (no barrier)
-    if constexpr (!PROG) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    int t0 = 0;
-    for (; t0 + D < nsteps; t0 += D) {
+    // one pass of the D slots (K = 512 D) runs as straight-line code: after a
+    // loop the compiler's count of the loads in flight restarts from zero, so
+    // every step would wait for all of them
+    if (nsteps == D) {
 #pragma unroll
-        for (int s = 0; s < D; ++s) body(std::true_type{}, s, t0 + s);
+        for (int s = 0; s < D; ++s) body(std::false_type{}, s, s);
+    } else {
+        int t0 = 0;
+        for (; t0 + D < nsteps; t0 += D) {
+#pragma unroll
+            for (int s = 0; s < D; ++s) body(std::true_type{}, s, t0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < D; ++s) body(std::false_type{}, s, t0 + s);
     }
-#pragma unroll
-    for (int s = 0; s < D; ++s) body(std::false_type{}, s, t0 + s);
 
     // ---- the waves' totals added in wave order.  Register i of column block j
     // holds row 4q + i of column nl + j; every wave leaves its four rows' values in
@@ -461,46 +421,32 @@ hipError_t run_skinny_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s)
     return run_skinny<NBW, 8, D, 16>(a, lds, dev, s);
 }
 
-template <int CPL, int D, int XM>
+template <int CPL, int D, int PPS>
 hipError_t run_skinny16(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
     static std::atomic<uint64_t> attr_set{0};
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!bit || !(attr_set.load() & bit)) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, XM>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, PPS>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyMaxLds);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit);
     }
     const unsigned blocks = (unsigned)((a.N + 16 * CPL - 1) / (16 * CPL));
-    skinny16_kernel<CPL, D, XM><<<dim3(blocks), dim3(512), lds, s>>>(a);
+    skinny16_kernel<CPL, D, PPS><<<dim3(blocks), dim3(512), lds, s>>>(a);
     return hipGetLastError();
 }
 
-// How x is staged, measured with cold weights at K = 4096 (us per call, all at
-// once / step by step): with four columns per lane step by step wins at every M
-// (N = 14336: M = 1 9.15 / 8.05, M = 8 9.88 / 9.09, M = 16 11.6 / 10.6); with
-// one or two only for 2 <= M <= 4 (N = 4096, M = 2: 5.01 / 4.60; N = 8192,
-// M = 4: 7.12 / 6.27), and all at once for M = 1 (4.15 / 4.60) and M > 4
-// (N = 8192, M = 16: 8.95 / 9.86).  Step by step takes ceil(M/4) pieces per lane
-// and step (three take four); all at once the fewest of 2, 16 or 32 per lane
-// that cover the wave's slice.
+// x pieces per lane and step: ceil(M/4) (the rows 4i + q, i < PPS).  Four
+// steps in flight instead of eight with three or four pieces, and with two at
+// four columns per lane, where eight spill registers (cold weights, N = 14336:
+// M = 5 7.8 us with four in flight against 8.1 with eight and the spill).
 template <int CPL, int D>
 hipError_t run_skinny16_x(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
-    if (CPL == 4 || (a.M >= 2 && a.M <= 4)) {
-        if (a.M <= 4) return run_skinny16<CPL, D, 1>(a, lds, dev, s);
-        if constexpr (CPL == 4) {
-            if (a.M <= 8) return run_skinny16<CPL, D, 2>(a, lds, dev, s);
-            // four pieces per lane keep four steps in flight (eight spill)
-            return run_skinny16<CPL, D == 8 ? 4 : D, 4>(a, lds, dev, s);
-        }
-    }
-    if constexpr (CPL != 4) {
-        const int64_t per_thread = ((int64_t)a.M * a.K / 4 + 511) / 512;
-        if (per_thread <= 2) return run_skinny16<CPL, D, -2>(a, lds, dev, s);
-        if (per_thread <= 16) return run_skinny16<CPL, D, -16>(a, lds, dev, s);
-        return run_skinny16<CPL, D, -32>(a, lds, dev, s);
-    }
-    return hipErrorInvalidValue;  // not reached: four columns per lane always go step by step
+    constexpr int D4 = D == 8 ? 4 : D;
+    if (a.M <= 4) return run_skinny16<CPL, D, 1>(a, lds, dev, s);
+    if (a.M <= 8) return run_skinny16<CPL, CPL == 4 ? D4 : D, 2>(a, lds, dev, s);
+    if (a.M <= 12) return run_skinny16<CPL, D4, 3>(a, lds, dev, s);
+    return run_skinny16<CPL, D4, 4>(a, lds, dev, s);
 }
 
 template <int CPL>
