@@ -25,8 +25,10 @@ hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t
 // the waves of each workgroup).
 hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
 
-// Skinny MFMA kernel for M <= kSkinnyMaxM whose x (as f16) fits in LDS.
+// Skinny MFMA kernels: for K % 1024 == 0 up to kSkinny16MaxM rows (x held two
+// steps at a time), otherwise up to kSkinnyMaxM rows whose x (as f16) fits in LDS.
 constexpr int64_t kSkinnyMaxM = 16;
+constexpr int64_t kSkinny16MaxM = 32;
 constexpr size_t kSkinnyMaxLds = 160 * 1024;  // all of gfx950's LDS per workgroup
 bool skinny_fits(const DevWeight &w, int64_t M);
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s);

@@ -2,7 +2,7 @@
 // (code-1)*d, the ternary GEMM of "oxibonsai-kernels 0.2.1 -- tests_gemm_tq2.rs"
 // on the f16 MFMA path (same operands and bound as the tiled kernel).
 //
-// For M <= 16 (M*K <= 65536) the whole of x fits in LDS as f16, so a workgroup stages it once
+// For few rows (up to 32, or 16 with M*K <= 65536) a workgroup keeps x in LDS as f16,
 // and its waves then run without barriers: each wave streams the code words of
 // the workgroup's output columns over its own eighth of K straight from HBM into
 // registers, several steps ahead, decodes them and issues MFMAs with A fragments
@@ -18,6 +18,7 @@
 
 #include <atomic>
 #include <type_traits>
+
 
 #include "decode.h"
 #include "internal.h"
@@ -212,13 +213,18 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
 // of D steps are in flight.  The loads go out step by step, x with its step's
 // words, so a step waits only for its own data (the memory counter retires in
 // issue order), and each step's x is rounded to f16 into LDS after the MFMAs of
-// the step before.  The wave reads only the x it stores itself, so no barrier
-// is needed, and the last D steps issue no further loads.  At the end the
-// waves' totals are added in wave order through LDS, as in skinny_kernel.
-template <int CPL, int D, int PPS>
+// the step before.  Each wave keeps the x of two steps in LDS (the one its
+// MFMAs read and the next), 16*RB rows of 64 k each, so up to 32 rows fit; it
+// reads only the x it stores itself, so no barrier is needed.  With RB = 2 row
+// blocks each decoded word feeds four MFMAs.  The last D steps issue no further
+// loads.  At the end the waves' totals are added in wave order through LDS, as
+// in skinny_kernel.
+template <int CPL, int D, int PPS, int RB>
 __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     constexpr int WK = 8;
     constexpr int SW = (CPL + 1) / 2;  // 32-bit words holding the lane's CPL scales
+    constexpr int XR = 16 * RB;        // rows of x a wave holds per step
+    constexpr int XS = 72;             // halves per row: 64 k and 8 of padding (16 rows hit all banks)
     typedef uint32_t uw __attribute__((ext_vector_type(CPL)));
     typedef uint32_t us __attribute__((ext_vector_type(SW)));
     typedef uint16_t us1;
@@ -262,22 +268,23 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
             }
         }
     };
-    // step t's x, rounded to f16 (nearest even), into LDS.  Rows past M hold
-    // row M-1's values and store them at row M-1 again (the same bits), so the
-    // stores need no branch: a branch would take the loads that feed them in,
-    // and its wait would then count every load in flight.
+    // step t's x, rounded to f16 (nearest even), into the wave's LDS half t % 2.
+    // Rows past M hold row M-1's values and store them at row M-1 again (the
+    // same bits), so the stores need no branch: a branch would take the loads
+    // that feed them in, and its wait would then count every load in flight.
+    _Float16 *xw = xs + wave * (2 * XR * XS);
     int xrow_s[PPS];
 #pragma unroll
     for (int i = 0; i < PPS; ++i) {
         const int r = 4 * i + q;
-        xrow_s[i] = xs_row(r < p.M ? r : p.M - 1, p.K) + kbeg + 4 * c;
+        xrow_s[i] = (r < p.M ? r : p.M - 1) * XS + 4 * c;
     }
     auto stage = [&](int slot, int t) {
 #pragma unroll
         for (int i = 0; i < PPS; ++i) {
             const h4 h = {(_Float16)xv[slot][i][0], (_Float16)xv[slot][i][1], (_Float16)xv[slot][i][2],
                           (_Float16)xv[slot][i][3]};
-            *reinterpret_cast<h4 *>(&xs[xrow_s[i] + 64 * t]) = h;
+            *reinterpret_cast<h4 *>(&xw[(t & 1) * (XR * XS) + xrow_s[i]]) = h;
         }
     };
 
@@ -289,16 +296,28 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
     }
     stage(0, 0);
 
-    f4 acc[CPL], blk[CPL];
+    f4 acc[RB][CPL], blk[RB][CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) acc[j] = f4{}, blk[j] = f4{};
-    const int arow = c < p.M ? c : p.M - 1;  // rows past M repeat row M-1; never stored
-    const _Float16 *xrow = xs + xs_row(arow, p.K) + kbeg + 16 * q;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) acc[rb][j] = f4{}, blk[rb][j] = f4{};
+    // A rows 16 rb + c; rows past M repeat row M-1 (never stored)
+    int arow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = 16 * rb + c;
+        arow[rb] = (r < p.M ? r : p.M - 1) * XS + 16 * q;
+    }
     // step t from slot s: the MFMAs, then the next step's x into LDS, then
     // (MORE) the loads of step t + D into the slot
     auto body = [&](auto more, int s, int t) {
-        const _Float16 *xa = xrow + t * 64;
-        const h8 a0 = *reinterpret_cast<const h8 *>(xa), a1 = *reinterpret_cast<const h8 *>(xa + 8);
+        const _Float16 *xh = xw + (t & 1) * (XR * XS);
+        h8 a0[RB], a1[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            a0[rb] = *reinterpret_cast<const h8 *>(xh + arow[rb]);
+            a1[rb] = *reinterpret_cast<const h8 *>(xh + arow[rb] + 8);
+        }
         h8 b1[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -307,10 +326,15 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
             const h8 b0 = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
             b1[j] = h8{pr[4].x, pr[4].y, pr[5].x, pr[5].y, pr[6].x, pr[6].y, pr[7].x, pr[7].y};
             // a block's first step starts its sums from zero
-            blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, (s & 1) ? blk[j] : f4{}, 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                blk[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[rb], b0, (s & 1) ? blk[rb][j] : f4{}, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) blk[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], blk[j], 0, 0, 0);
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                blk[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[rb], b1[j], blk[rb][j], 0, 0, 0);
         if (s & 1) {  // the block's second step: add d * (block sum) to the total
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
@@ -318,7 +342,9 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
                 const uint32_t dw = dv[s][j >> 1];
                 const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? dw >> 16 : dw & 0xFFFFu));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(d, blk[j][i], acc[j][i]);
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rb][j][i] = __builtin_fmaf(d, blk[rb][j][i], acc[rb][j][i]);
             }
         }
         if (s + 1 < D)
@@ -343,25 +369,28 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
         for (int s = 0; s < D; ++s) body(std::false_type{}, s, t0 + s);
     }
 
-    // ---- the waves' totals added in wave order.  Register i of column block j
-    // holds row 4q + i of column nl + j; every wave leaves its four rows' values in
-    // LDS (the lane's CPL columns side by side), then waves 0..3 each add one
-    // register's over the waves and store the row's CPL columns.
+    // ---- the waves' totals added in wave order.  Register i of row block rb
+    // and column block j holds row 16 rb + 4q + i of column nl + j; every wave
+    // leaves its values in LDS (the lane's CPL columns side by side), then wave
+    // w adds (rb, i) = (w / 4, w % 4) over the waves and stores the row's CPL
+    // columns.
     __syncthreads();
     fv *red = reinterpret_cast<fv *>(xs);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fv v;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) v[j] = acc[j][i];
-        red[(wave * 4 + i) * 64 + lane] = v;
-    }
+        for (int i = 0; i < 4; ++i) {
+            fv v;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) v[j] = acc[rb][j][i];
+            red[(wave * 4 * RB + 4 * rb + i) * 64 + lane] = v;
+        }
     __syncthreads();
-    if (wave < 4) {
-        const int i = wave, row = 4 * q + i;
-        fv v = red[i * 64 + lane];
+    if (wave < 4 * RB) {
+        const int row = 16 * (wave >> 2) + 4 * q + (wave & 3);
+        fv v = red[wave * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < WK; ++w) v += red[(w * 4 + i) * 64 + lane];
+        for (int w = 1; w < WK; ++w) v += red[(w * 4 * RB + wave) * 64 + lane];
         if (row < p.M) {
             float *yr = p.y + (int64_t)row * p.N;
             if (p.N % CPL == 0 && nl + CPL <= p.N) {
@@ -394,18 +423,19 @@ hipError_t run_skinny(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
 }  // namespace
 
 bool skinny_fits(const DevWeight &w, int64_t M) {
-    // eight waves of 64 k-wide steps: K % 512 == 0; x staged in one round of at
-    // most 32 pieces per thread (M*K/4 <= 512*32) and, as f16 with padded rows,
-    // within the LDS of a workgroup
-    if (M < 1 || M > kSkinnyMaxM || w.K % 512 != 0 || M * w.K > 4 * 512 * 32 ||
-        (size_t)M * (w.K + 8) * 2 > kSkinnyMaxLds)
+    if (M < 1) return false;
+    // skinny16_kernel (K % 1024 == 0; x held two steps at a time): up to 32 rows
+    // at any N and K.  Measured with cold weights at K = 4096, N = 14336, M = 9..16
+    // took 10.9-11.7 us (x staged whole) against the tiled kernel's 13.4.
+    if (w.K % 1024 == 0) return M <= kSkinny16MaxM;
+    // skinny_kernel: eight waves of 64 k-wide steps (K % 512 == 0); x staged in
+    // one round of at most 32 pieces per thread (M*K/4 <= 512*32) and, as f16
+    // with padded rows, within the LDS of a workgroup; more than 16 pieces per
+    // thread only with 32-column workgroups (N <= 8192), where M = 12..16 took
+    // 10.1-10.3 us against the tiled kernel's 13.1 at N = 4096, but 14.3 against
+    // 13.7-13.8 at N = 14336.
+    if (M > kSkinnyMaxM || w.K % 512 != 0 || M * w.K > 4 * 512 * 32 || (size_t)M * (w.K + 8) * 2 > kSkinnyMaxLds)
         return false;
-    // skinny16_kernel (K % 1024 == 0) at any N: measured with cold weights at
-    // K = 4096, N = 14336, M = 9..16 take 10.9-11.7 us against the tiled kernel's
-    // 13.4.  skinny_kernel: more than 16 pieces per thread only with 32-column
-    // workgroups (N <= 8192), where M = 12..16 took 10.1-10.3 us against 13.1 at
-    // N = 4096, but 14.3 against 13.7-13.8 at N = 14336.
-    if (w.K % 1024 == 0) return true;
     return M * w.K <= 4 * 512 * 16 || (w.N + 31) / 32 <= 256;
 }
 
@@ -421,43 +451,47 @@ hipError_t run_skinny_u(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s)
     return run_skinny<NBW, 8, D, 16>(a, lds, dev, s);
 }
 
-template <int CPL, int D, int PPS>
-hipError_t run_skinny16(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+template <int CPL, int D, int PPS, int RB>
+hipError_t run_skinny16(const SkinnyArgs &a, int dev, hipStream_t s) {
     static std::atomic<uint64_t> attr_set{0};
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!bit || !(attr_set.load() & bit)) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, PPS>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny16_kernel<CPL, D, PPS, RB>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyMaxLds);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit);
     }
+    // LDS: each wave's two steps of x (16 RB rows of 72 halves), later the eight
+    // waves' 4 RB rows of CPL columns
+    const size_t xb = (size_t)8 * 2 * 16 * RB * 72 * 2, rb = (size_t)8 * 4 * RB * 64 * CPL * 4;
+    const size_t lds = xb > rb ? xb : rb;
     const unsigned blocks = (unsigned)((a.N + 16 * CPL - 1) / (16 * CPL));
-    skinny16_kernel<CPL, D, PPS><<<dim3(blocks), dim3(512), lds, s>>>(a);
+    skinny16_kernel<CPL, D, PPS, RB><<<dim3(blocks), dim3(512), lds, s>>>(a);
     return hipGetLastError();
 }
 
-// x pieces per lane and step: ceil(M/4) (the rows 4i + q, i < PPS).  Four
-// steps in flight instead of eight with three or four pieces, and with two at
-// four columns per lane, where eight spill registers (cold weights, N = 14336:
+// x pieces per lane and step: ceil(M/4) (the rows 4i + q, i < PPS), rounded up
+// to 6 or 8 past 16 rows (two row blocks).  Four steps in flight instead of
+// eight with three or four pieces, and with two at four columns per lane, and
+// two with two row blocks, where more spill registers (cold weights, N = 14336:
 // M = 5 7.8 us with four in flight against 8.1 with eight and the spill).
 template <int CPL, int D>
-hipError_t run_skinny16_x(const SkinnyArgs &a, size_t lds, int dev, hipStream_t s) {
+hipError_t run_skinny16_x(const SkinnyArgs &a, int dev, hipStream_t s) {
     constexpr int D4 = D == 8 ? 4 : D;
-    if (a.M <= 4) return run_skinny16<CPL, D, 1>(a, lds, dev, s);
-    if (a.M <= 8) return run_skinny16<CPL, CPL == 4 ? D4 : D, 2>(a, lds, dev, s);
-    if (a.M <= 12) return run_skinny16<CPL, D4, 3>(a, lds, dev, s);
-    return run_skinny16<CPL, D4, 4>(a, lds, dev, s);
+    if (a.M <= 4) return run_skinny16<CPL, D, 1, 1>(a, dev, s);
+    if (a.M <= 8) return run_skinny16<CPL, CPL == 4 ? D4 : D, 2, 1>(a, dev, s);
+    if (a.M <= 12) return run_skinny16<CPL, D4, 3, 1>(a, dev, s);
+    if (a.M <= 16) return run_skinny16<CPL, D4, 4, 1>(a, dev, s);
+    if (a.M <= 24) return run_skinny16<CPL, 2, 6, 2>(a, dev, s);
+    return run_skinny16<CPL, 2, 8, 2>(a, dev, s);
 }
 
 template <int CPL>
 hipError_t run_skinny16_d(const SkinnyArgs &a, int dev, hipStream_t s) {
-    // LDS: x as f16 (padded rows), later the eight waves' four rows of CPL columns
-    const size_t xb = (size_t)a.M * (a.K + 8) * 2, rb = (size_t)8 * 4 * 64 * CPL * 4;
-    const size_t lds = xb > rb ? xb : rb;
     const int steps = a.K / 512;  // per wave: even
-    if (steps % 8 == 0) return run_skinny16_x<CPL, 8>(a, lds, dev, s);
-    if (steps % 4 == 0) return run_skinny16_x<CPL, 4>(a, lds, dev, s);
-    return run_skinny16_x<CPL, 2>(a, lds, dev, s);
+    if (steps % 8 == 0) return run_skinny16_x<CPL, 8>(a, dev, s);
+    if (steps % 4 == 0) return run_skinny16_x<CPL, 4>(a, dev, s);
+    return run_skinny16_x<CPL, 2>(a, dev, s);
 }
 
 // Columns per lane of skinny16_kernel: the widest that still gives about three

@@ -46,6 +46,9 @@ CASES = [
     ("skinny 16x16x32, four columns per lane, N % 4 == 2", "mfma", (2, 12), 12302, 1024),
     ("skinny 16x16x32, four columns per lane, two and four pieces per step (M=13: two passes)", "mfma", (6, 13),
      12302, 4096),
+    ("skinny 16x16x32, two row blocks (M=20: six pieces per step, M=32: eight; two passes)", "mfma", (20, 32),
+     12302, 2048),
+    ("skinny 16x16x32, two row blocks, one column per lane", "mfma", (17,), 1000, 4096),
     ("skinny 32x32x16, K not a multiple of 1024", "mfma", (4, 12), 1000, 1536),
     ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),

@@ -1,11 +1,12 @@
 """GPU parity of the MFMA path's small-M kernels with the oracle.
 
-Up to 16 rows the MFMA path runs a skinny kernel: x is staged whole in LDS and
-eight waves each take one eighth of K, their partial tiles added in wave order.
-With K a multiple of 1024 that is the 16x16x32 kernel (each lane one, two or four
-output columns by N, each block's sum scaled by d); other K (a multiple of 512,
-with M*K <= 32768, or <= 65536 when N <= 8192) take the 32x32x16 skinny kernel
-(d folded into the f16 operand).  Other M <= 32 take 32x64 tiles and 33 <= M <= 64
+With K a multiple of 1024, up to 32 rows run the 16x16x32 skinny kernel: eight
+waves each take one eighth of K, staging their x into LDS step by step (two steps
+held, one or two 16-row blocks), each lane one, two or four output columns by N,
+each block's sum scaled by d, the waves' partial tiles added in wave order.  Other
+K (a multiple of 512, up to 16 rows with M*K <= 32768, or <= 65536 when N <= 8192)
+take the 32x32x16 skinny kernel (x staged whole, d folded into the f16 operand).
+Other M <= 32 take 32x64 tiles and 33 <= M <= 64
 take 64x64 tiles, whose waves split each step's K (four ways; with K/128 a
 multiple of 8, each of the four takes two 64-wide slices of a 512-wide step;
 two ways when K has few blocks) and add their partial tiles in a fixed order at
@@ -33,9 +34,9 @@ def torch():
 
 
 # K/128 = 32 (multiple of 8: four k groups of two slices), 12 (multiple of 4
-# only: four k groups), 6 (even: two k groups), 3 (odd: 256-column tiles).  For
-# M <= 16, K=4096 runs the 16x16x32 skinny kernel, K=1536 the 32x32x16 one (M*K
-# <= 65536 at this N) and the others the tiled kernels.
+# only: four k groups), 6 (even: two k groups), 3 (odd: 256-column tiles).  K=4096
+# runs the 16x16x32 skinny kernel up to M=32, K=1536 the 32x32x16 one up to M=16
+# (M*K <= 65536 at this N), and the others the tiled kernels.
 KS = [4096, 1536, 768, 384]
 
 
