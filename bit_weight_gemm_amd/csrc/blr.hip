@@ -375,8 +375,10 @@ __global__ __launch_bounds__(256) void blr_dyc_kernel(DycArgs q) {
 
 // out[n] = f32(out[n] + f32(sum over row blocks b in order of part[b][n])) for the
 // three gradients of a path (dh: d_out columns, dl: r, dg: d_in), one thread per
-// column; the loads of a group of blocks are independent, so they go out
-// together, then are added in order.
+// column.  Each gradient's columns start a workgroup, so a workgroup's gradient is
+// the same for all its threads and its pointers come from scalar loads; out[n] is
+// loaded together with the partial sums of a group of blocks, which are then
+// added in order.
 struct FinishJob {
     const float *part;
     float *out;
@@ -385,16 +387,20 @@ struct FinishJob {
 struct FinishArgs {
     FinishJob job[3];
     int64_t blocks;
+    unsigned wg1, wg2;  // first workgroups of gradients 1 and 2
 };
 
 __global__ __launch_bounds__(256) void blr_finish_kernel(FinishArgs q) {
 #pragma clang fp contract(off)
-    int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int j = 0;
-    while (j < 3 && n >= q.job[j].N) n -= q.job[j++].N;
-    if (j == 3) return;
+    const unsigned wg = blockIdx.x;
+    const int j = wg >= q.wg2 ? 2 : wg >= q.wg1 ? 1 : 0;
+    const unsigned first = j == 2 ? q.wg2 : j == 1 ? q.wg1 : 0u;
     const float *__restrict__ part = q.job[j].part;
+    float *__restrict__ out = q.job[j].out;
     const int64_t N = q.job[j].N;
+    const int64_t n = (int64_t)(wg - first) * 256 + threadIdx.x;
+    if (n >= N) return;
+    const float o = out[n];
     float s = 0.0f;
     int64_t b = 0;
     for (; b + 16 <= q.blocks; b += 16) {
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(256) void blr_finish_kernel(FinishArgs q) {
         for (int i = 0; i < 16; ++i) s = s + v[i];
     }
     for (; b < q.blocks; ++b) s = s + part[b * N + n];
-    q.job[j].out[n] = q.job[j].out[n] + s;
+    out[n] = o + s;
 }
 
 }  // namespace
@@ -452,8 +458,10 @@ static hipError_t backward_tail(const BlrBwdPlan &pb, const uint32_t *bits_u, co
     q.job[1] = FinishJob{part_dl, dl, r};
     q.job[2] = FinishJob{part_dg, dg, d_in};
     q.blocks = pb.blocks;
-    const int64_t cols = d_out + r + d_in;
-    blr_finish_kernel<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s>>>(q);
+    const unsigned w0 = (unsigned)((d_out + 255) / 256), w1 = (unsigned)((r + 255) / 256),
+                   w2 = (unsigned)((d_in + 255) / 256);
+    q.wg1 = w0, q.wg2 = w0 + w1;
+    blr_finish_kernel<<<dim3(w0 + w1 + w2), dim3(256), 0, s>>>(q);
     return hipGetLastError();
 }
 
