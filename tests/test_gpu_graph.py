@@ -7,7 +7,8 @@ both paths, a binary low-rank forward on the library's workspace (at a size
 whose first product is one launch, and at one whose contraction is split over
 workgroups with a launch that adds the chunks), one on the fixed scratch
 (blr_forward_noalloc) and the backward from saved activations is
-replayed several times, with other eager library work and synchronisations in
+replayed several times (with the ternary GEMM also at M=8 and M=24, the skinny
+kernel with one and two row blocks), with other eager library work and synchronisations in
 between, and every replay must give the eager results bit for bit; after the
 inputs are overwritten in place, a replay must give the eager results on the
 new inputs.
@@ -34,11 +35,13 @@ def test_graph_replays_match_eager(torch):
     w = bw.tq2_upload(aos, n, k)
     x1 = to_dev(wl.random_x(1, k, 32))
     x100 = to_dev(wl.random_x(100, k, 33))
+    x8, x24 = to_dev(wl.random_x(8, k, 41)), to_dev(wl.random_x(24, k, 42))
     d = wl.blr_inputs(m=70, d_in=384, d_out=256, r=128, index=34)
     bu, bv = bits_dev(d["bits_u"]), bits_dev(d["bits_v"])
     h, l, g, xb = to_dev(d["h"]), to_dev(d["l"]), to_dev(d["g"]), to_dev(d["x"])
     dy = to_dev((np.random.default_rng(35).standard_normal((70, 256)) * 1e-3).astype(np.float32))
     y1, y100 = torch.empty((1, n), device="cuda"), torch.empty((100, n), device="cuda")
+    y8, y24 = torch.empty((8, n), device="cuda"), torch.empty((24, n), device="cuda")
     yb, yn = torch.empty((70, 256), device="cuda"), torch.empty((70, 256), device="cuda")
     ys = torch.empty((70, 256), device="cuda")
     saved = torch.empty(bw.blr_saved_size(1, 70, 384, 256, 128), dtype=torch.uint8, device="cuda")
@@ -53,6 +56,8 @@ def test_graph_replays_match_eager(torch):
     def work(s):
         bw.tq2_gemm_path(w, x1, y1, bw.TQ2_PATH_F32, stream=s)
         bw.tq2_gemm_path(w, x100, y100, bw.TQ2_PATH_MFMA, stream=s)
+        bw.tq2_gemm_path(w, x8, y8, bw.TQ2_PATH_MFMA, stream=s)
+        bw.tq2_gemm_path(w, x24, y24, bw.TQ2_PATH_MFMA, stream=s)
         bw.blr_forward(bu, bv, h, l, g, xb, yb, stream=s)
         bw.blr_forward(*b2, y2, stream=s)
         bw._check(bw.lib().blr_forward_noalloc(
@@ -62,7 +67,7 @@ def test_graph_replays_match_eager(torch):
         bw.blr_forward_paths_save(P(bu), P(bv), P(h), P(l), P(g), xb, ys, saved, stream=s)
         bw.blr_backward_paths_saved(P(bu), P(bv), P(h), P(l), P(g), xb, dy, *grads, saved, dx=dx, stream=s)
 
-    outs = (y1, y100, yb, yn, ys, dx, y2)
+    outs = (y1, y100, yb, yn, ys, dx, y2, y8, y24)
 
     def eager():
         for t in grads:
@@ -105,6 +110,7 @@ def test_graph_replays_match_eager(torch):
     # new inputs in place: the replay must follow them
     x1.copy_(to_dev(wl.random_x(1, k, 36)))
     x100.copy_(to_dev(wl.random_x(100, k, 37)))
+    x8.copy_(to_dev(wl.random_x(8, k, 43)))
     xb.copy_(to_dev(wl.random_x(70, 384, 38)))
     b2[5].copy_(to_dev(wl.random_x(300, 4096, 40)))
     torch.cuda.synchronize()
