@@ -50,6 +50,9 @@ CASES = [
      12302, 2048),
     ("skinny 16x16x32, two row blocks, one column per lane", "mfma", (17,), 1000, 4096),
     ("skinny 32x32x16, K not a multiple of 1024", "mfma", (4, 12), 1000, 1536),
+    ("skinny 16x16x32, K=32768: many passes of the load slots", "mfma", (1, 3, 8, 20), 300, 32768),
+    ("gemv_mt, K=32768: eight 4096-wide passes", "f32", (1, 4), 300, 32768),
+    ("64x64 tiles, K=32768", "mfma", (40,), 300, 32768),
     ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
     ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
