@@ -192,8 +192,9 @@ __global__ __launch_bounds__(WK * 64) void skinny_kernel(SkinnyArgs p) {
     }
 }
 
-// ---- the same product on v_mfma_f32_16x16x32_f16 (no rows wasted at M <= 16),
-// for K a multiple of 1024 (eight waves, each owning whole 128-wide blocks).
+// ---- the same product on v_mfma_f32_16x16x32_f16 (16-row MFMA blocks, so no rows
+// are wasted when M is a multiple of 16), for up to 32 rows and K a multiple of
+// 1024 (eight waves, each owning whole 128-wide blocks).
 //
 // Lane l = 16q + c holds MFMA row/column slot c and k octet q.  It owns the CPL
 // adjacent weight rows (output columns) n0 + CPL*c + j, j < CPL: their code
