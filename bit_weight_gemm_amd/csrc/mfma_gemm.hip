@@ -55,13 +55,13 @@ hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_
     // Small M: 64-column tiles whose four waves of each column half split the
     // step's K four ways (two ways when K has too few blocks), so N/64
     // workgroups of eight waves stream the weight.  When K/128 is a multiple of
-    // 8, each wave takes two 64-wide slices of a 512-wide step: with so little
-    // MFMA work per step, fewer steps (and barriers) matter most.  Up to 32
-    // rows, A comes through a buffer resource, so the rows past M cost no memory
+    // 8 (33 to 64 rows; up to 32 rows such K goes to the skinny kernel), each
+    // wave takes two 64-wide slices of a 512-wide step: with so little MFMA
+    // work per step, fewer steps (and barriers) matter most.  Up to 32 rows, A
+    // comes through a buffer resource, so the rows past M cost no memory
     // traffic.
     const int64_t kb = w.K / kBlock;
     if (M <= 32 && M * w.K * 4 < ((int64_t)1 << 31)) {
-        if (kb % 8 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, true, kEpiStore, 2, 1, 2>(p, s);
         if (kb % 4 == 0) return run_gemm<32, 64, 1, 2, 4, 2, kABuf, true, kEpiStore>(p, s);
         if (kb % 2 == 0) return run_gemm<32, 64, 1, 2, 2, 2, kABuf, true, kEpiStore>(p, s);
     } else if (M <= 64) {

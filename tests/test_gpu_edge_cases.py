@@ -53,7 +53,7 @@ CASES = [
     ("skinny 16x16x32, K=32768: many passes of the load slots", "mfma", (1, 3, 8, 20), 300, 32768),
     ("gemv_mt, K=32768: eight 4096-wide passes", "f32", (1, 4), 300, 32768),
     ("64x64 tiles, K=32768", "mfma", (40,), 300, 32768),
-    ("32x64 tiles, 512-wide steps", "mfma", (20,), 1000, 4096),
+    ("skinny 16x16x32, two row blocks, two columns per lane", "mfma", (20,), 9000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
     ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
     ("64x64 tiles, 512-wide steps", "mfma", (40,), 1000, 4096),
