@@ -30,7 +30,7 @@ def torch():
 
 
 def test_graph_replays_match_eager(torch):
-    note("[graph] capture of tq2_gemm (both paths), blr_forward, blr_forward_noalloc, backward from saved")
+    note("[graph] capture of tq2_gemm (both paths), blr_forward, blr_forward_noalloc, both backwards")
     aos, n, k = wl.random_weight(1000, 1024, 31), 1000, 1024
     w = bw.tq2_upload(aos, n, k)
     x1 = to_dev(wl.random_x(1, k, 32))
@@ -46,7 +46,8 @@ def test_graph_replays_match_eager(torch):
     ys = torch.empty((70, 256), device="cuda")
     saved = torch.empty(bw.blr_saved_size(1, 70, 384, 256, 128), dtype=torch.uint8, device="cuda")
     grads = [torch.zeros((1, m), device="cuda") for m in (256, 128, 384)]
-    dx = torch.empty((70, 384), device="cuda")
+    grads_r = [torch.zeros((1, m), device="cuda") for m in (256, 128, 384)]
+    dx, dx_r = torch.empty((70, 384), device="cuda"), torch.empty((70, 384), device="cuda")
     P = lambda t: t[None]  # noqa: E731  (one path)
     # first product split four ways over d_in (10 x 4 tiles of 32 x 128)
     d2 = wl.blr_inputs(m=300, d_in=4096, d_out=256, r=512, index=39)
@@ -66,16 +67,18 @@ def test_graph_replays_match_eager(torch):
             bw._dev(yn, torch.float32, "y"), 70, 384, 256, 128, bw._stream(s)), "blr_forward_noalloc")
         bw.blr_forward_paths_save(P(bu), P(bv), P(h), P(l), P(g), xb, ys, saved, stream=s)
         bw.blr_backward_paths_saved(P(bu), P(bv), P(h), P(l), P(g), xb, dy, *grads, saved, dx=dx, stream=s)
+        bw.blr_backward_paths(P(bu), P(bv), P(h), P(l), P(g), xb, dy, *grads_r, dx=dx_r, stream=s)
 
-    outs = (y1, y100, yb, yn, ys, dx, y2, y8, y24)
+    outs = (y1, y100, yb, yn, ys, dx, y2, y8, y24, dx_r)
+    accum = grads + grads_r  # accumulated in place: cleared before each run
 
     def eager():
-        for t in grads:
+        for t in accum:
             t.zero_()
         s = torch.cuda.current_stream()
         work(s)
         torch.cuda.synchronize()
-        return [o.cpu().numpy().copy() for o in outs] + [t.cpu().numpy().copy() for t in grads]
+        return [o.cpu().numpy().copy() for o in outs] + [t.cpu().numpy().copy() for t in accum]
 
     want = eager()                        # warms the library's workspaces up
     side = torch.cuda.Stream()
@@ -85,7 +88,7 @@ def test_graph_replays_match_eager(torch):
     torch.cuda.synchronize()
     allocs = bw.tq2_workspace_allocs()
     graph = torch.cuda.CUDAGraph()
-    for t in grads:
+    for t in accum:
         t.zero_()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=side):
@@ -93,13 +96,13 @@ def test_graph_replays_match_eager(torch):
     assert bw.tq2_workspace_allocs() == allocs   # nothing allocated while capturing
 
     def replay():
-        for t in grads:
+        for t in accum:
             t.zero_()
         torch.cuda.synchronize()
         with torch.cuda.stream(side):
             graph.replay()
         torch.cuda.synchronize()
-        return [o.cpu().numpy().copy() for o in outs] + [t.cpu().numpy().copy() for t in grads]
+        return [o.cpu().numpy().copy() for o in outs] + [t.cpu().numpy().copy() for t in accum]
 
     for rep in range(4):
         got = replay()
