@@ -24,6 +24,8 @@ hipError_t launch_gemv_f32(const DevWeight &w, const float *x, float *y, int64_t
 // MFMA path (any M; small M uses 64-column tiles with the K range split over
 // the waves of each workgroup).
 hipError_t launch_gemm_mfma(const DevWeight &w, const float *x, float *y, int64_t M, hipStream_t s);
+// Compute units of the current device (256 if the query fails), cached per device.
+int device_cus();
 
 // Skinny MFMA kernels: for K % 1024 == 0 up to kSkinny16MaxM rows (x held two
 // steps at a time), otherwise up to kSkinnyMaxM rows whose x (as f16) fits in LDS.

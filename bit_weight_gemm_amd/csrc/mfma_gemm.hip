@@ -10,7 +10,7 @@ namespace tq2 {
 static int mfma_stages(int64_t K) { return (K / BK) % 4 == 0 ? 4 : 2; }
 
 // Compute units of the current device, cached per device ordinal.
-static int device_cus() {
+int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;

@@ -354,12 +354,31 @@ __global__ __launch_bounds__(512) void skinny16_kernel(SkinnyArgs p) {
             stage(0, t + 1);
         if constexpr (decltype(more)::value) load(s, t + D);
     };
-    // one pass of the D slots (K = 512 D) runs as straight-line code: after a
+    // One pass of the D slots (K = 512 D) runs as straight-line code: after a
     // loop the compiler's count of the loads in flight restarts from zero, so
-    // every step would wait for all of them
+    // every step would wait for all of them.  Two or four passes are unrolled
+    // too: at a loop's entry the compiler copies the prefetched registers into
+    // the loop's own, and each copy waits for its load, so the first step would
+    // start only once all D steps had arrived (cold weights, K = 4096, N = 14336:
+    // M = 8 8.37 -> 7.98 us, M = 16 10.34 -> 9.78, M = 32 13.64 -> 13.23; N = 4096,
+    // M = 32 9.98 -> 8.65).  With one column per lane and one row block the loop
+    // stays (N = 4096, M = 12 and 16 were 0.1-0.26 us slower unrolled).
+    constexpr bool UNROLL = CPL >= 2 || RB == 2;
     if (nsteps == D) {
 #pragma unroll
         for (int s = 0; s < D; ++s) body(std::false_type{}, s, s);
+    } else if (UNROLL && nsteps == 2 * D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) body(std::true_type{}, s, s);
+#pragma unroll
+        for (int s = 0; s < D; ++s) body(std::false_type{}, s, D + s);
+    } else if (UNROLL && nsteps == 4 * D) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+            for (int s = 0; s < D; ++s) body(std::true_type{}, s, u * D + s);
+#pragma unroll
+        for (int s = 0; s < D; ++s) body(std::false_type{}, s, 3 * D + s);
     } else {
         int t0 = 0;
         for (; t0 + D < nsteps; t0 += D) {
@@ -495,16 +514,21 @@ hipError_t run_skinny16_d(const SkinnyArgs &a, int dev, hipStream_t s) {
     return run_skinny16_x<CPL, 2>(a, dev, s);
 }
 
-// Columns per lane of skinny16_kernel: the widest that still gives about three
-// workgroups for every four CUs (each workgroup stages all of x, so more
-// workgroups than that only add x traffic).  Measured with cold weights at
-// K = 4096: M = 8, N = 14336 takes 10.3 us with four columns per lane (224
-// workgroups), 12.8 with two, 13.9 with one; M = 1, N = 4096 takes 4.1 us with
-// one (256 workgroups), 6.0 with two and 8.3 with four.
+// Columns per lane of skinny16_kernel: the fewest (1, 2 or 4) that keep the
+// workgroups within one round of one per CU, since a second round costs about
+// as much as the first; past 4 * 16 * CUs columns, four.  More columns per lane
+// mean fewer workgroups, each streaming more code words, but every workgroup
+// stages all of x, so more workgroups than CUs add x traffic and a round.
+// Measured with cold weights at K = 4096 (us; in brackets the rule that took
+// the widest with at least 192 workgroups): N = 9000, M = 8 7.6 (10.65, two columns
+// per lane, 282 workgroups), M = 32 12.7 (19.9); N = 5000, M = 16 8.0 (11.1,
+// one column per lane, 313 workgroups); M = 8, N = 14336 takes 10.3 us with
+// four columns per lane (224 workgroups), 12.8 with two, 13.9 with one.
 static int skinny16_columns(int64_t N) {
-    for (int cpl = 4; cpl > 1; cpl /= 2)
-        if ((N + 16 * cpl - 1) / (16 * cpl) >= 192) return cpl;
-    return 1;
+    const int cus = device_cus();
+    for (int cpl = 1; cpl < 4; cpl *= 2)
+        if ((N + 16 * cpl - 1) / (16 * cpl) <= cus) return cpl;
+    return 4;
 }
 
 hipError_t launch_skinny(const DevWeight &w, const float *x, float *y, int64_t M, int dev, hipStream_t s) {

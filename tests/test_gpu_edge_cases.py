@@ -42,7 +42,7 @@ CASES = [
      1000, 4096),
     ("skinny 16x16x32, one column per lane, two passes of eight steps (M=3 step by step)", "mfma", (1, 3, 5),
      1000, 8192),
-    ("skinny 16x16x32, two columns per lane (M=3 step by step, M=12 all at once)", "mfma", (3, 12), 9000, 2048),
+    ("skinny 16x16x32, two columns per lane (M=3 step by step, M=12 all at once)", "mfma", (3, 12), 6000, 2048),
     ("skinny 16x16x32, four columns per lane, N % 4 == 2", "mfma", (2, 12), 12302, 1024),
     ("skinny 16x16x32, four columns per lane, two and four pieces per step (M=13: two passes)", "mfma", (6, 13),
      12302, 4096),
@@ -51,9 +51,11 @@ CASES = [
     ("skinny 16x16x32, two row blocks, one column per lane", "mfma", (17,), 1000, 4096),
     ("skinny 32x32x16, K not a multiple of 1024", "mfma", (4, 12), 1000, 1536),
     ("skinny 16x16x32, K=32768: many passes of the load slots", "mfma", (1, 3, 8, 20), 300, 32768),
+    ("skinny 16x16x32, K=8192: two and four passes unrolled", "mfma", (3, 12), 6000, 8192),
     ("gemv_mt, K=32768: eight 4096-wide passes", "f32", (1, 4), 300, 32768),
     ("64x64 tiles, K=32768", "mfma", (40,), 300, 32768),
-    ("skinny 16x16x32, two row blocks, two columns per lane", "mfma", (20,), 9000, 4096),
+    ("skinny 16x16x32, two row blocks, two columns per lane", "mfma", (20,), 6000, 4096),
+    ("skinny 16x16x32, four columns per lane in one round of 141 workgroups", "mfma", (8, 32), 9000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
     ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
     ("64x64 tiles, 512-wide steps", "mfma", (40,), 1000, 4096),
