@@ -519,11 +519,12 @@ hipError_t run_skinny16_d(const SkinnyArgs &a, int dev, hipStream_t s) {
 // as much as the first; past 4 * 16 * CUs columns, four.  More columns per lane
 // mean fewer workgroups, each streaming more code words, but every workgroup
 // stages all of x, so more workgroups than CUs add x traffic and a round.
-// Measured with cold weights at K = 4096 (us; in brackets the rule that took
-// the widest with at least 192 workgroups): N = 9000, M = 8 7.6 (10.65, two columns
-// per lane, 282 workgroups), M = 32 12.7 (19.9); N = 5000, M = 16 8.0 (11.1,
-// one column per lane, 313 workgroups); M = 8, N = 14336 takes 10.3 us with
-// four columns per lane (224 workgroups), 12.8 with two, 13.9 with one.
+// Measured with cold weights at K = 4096 (us; in brackets the earlier rule,
+// the widest with at least 192 workgroups): N = 9000, M = 8 7.6 (10.65, two
+// columns per lane, 282 workgroups), M = 32 12.7 (19.9); N = 5000, M = 16 8.0
+// (11.1, one column per lane, 313 workgroups).  An earlier form of the kernel
+// (x staged all at once) took 10.3 us at M = 8, N = 14336 with four columns per
+// lane (224 workgroups), 12.8 with two and 13.9 with one.
 static int skinny16_columns(int64_t N) {
     const int cus = device_cus();
     for (int cpl = 1; cpl < 4; cpl *= 2)
