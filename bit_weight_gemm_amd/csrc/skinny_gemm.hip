@@ -491,15 +491,18 @@ hipError_t run_skinny16(const SkinnyArgs &a, int dev, hipStream_t s) {
 }
 
 // x pieces per lane and step: ceil(M/4) (the rows 4i + q, i < PPS), rounded up
-// to 6 or 8 past 16 rows (two row blocks).  Four steps in flight instead of
-// eight with three or four pieces, and with two at four columns per lane, and
-// two with two row blocks, where more spill registers (cold weights, N = 14336:
-// M = 5 7.8 us with four in flight against 8.1 with eight and the spill).
+// to 6 or 8 past 16 rows (two row blocks).  Steps in flight: at most four from
+// five rows on and with four columns per lane, and two with two row blocks,
+// where more spill registers or measured slower (cold weights, K = 4096:
+// N = 14336, M = 1 and 4 7.5 -> 7.0 and 7.9 -> 7.1 us with four instead of
+// eight, M = 5 7.8 against 8.1; M = 8 at N = 4096 5.07 -> 4.91, at N = 6000
+// 6.25 -> 6.14); up to four rows with one or two columns per lane keep eight
+// (N = 4096, M = 1: 3.95 against 4.25 us with four).
 template <int CPL, int D>
 hipError_t run_skinny16_x(const SkinnyArgs &a, int dev, hipStream_t s) {
     constexpr int D4 = D == 8 ? 4 : D;
-    if (a.M <= 4) return run_skinny16<CPL, D, 1, 1>(a, dev, s);
-    if (a.M <= 8) return run_skinny16<CPL, CPL == 4 ? D4 : D, 2, 1>(a, dev, s);
+    if (a.M <= 4) return run_skinny16<CPL, CPL == 4 ? D4 : D, 1, 1>(a, dev, s);
+    if (a.M <= 8) return run_skinny16<CPL, D4, 2, 1>(a, dev, s);
     if (a.M <= 12) return run_skinny16<CPL, D4, 3, 1>(a, dev, s);
     if (a.M <= 16) return run_skinny16<CPL, D4, 4, 1>(a, dev, s);
     if (a.M <= 24) return run_skinny16<CPL, 2, 6, 2>(a, dev, s);
