@@ -55,7 +55,7 @@ CASES = [
     ("gemv_mt, K=32768: eight 4096-wide passes", "f32", (1, 4), 300, 32768),
     ("64x64 tiles, K=32768", "mfma", (40,), 300, 32768),
     ("skinny 16x16x32, two row blocks, two columns per lane", "mfma", (20,), 6000, 4096),
-    ("skinny 16x16x32, four columns per lane in one round of 141 workgroups", "mfma", (8, 32), 9000, 4096),
+    ("skinny 16x16x32, four columns per lane in one round of 141 workgroups", "mfma", (1, 4, 8, 32), 9000, 4096),
     ("32x64 tiles, four k groups", "mfma", (24,), 1000, 1536),
     ("32x64 tiles, two k groups", "mfma", (24,), 1000, 768),
     ("64x64 tiles, 512-wide steps", "mfma", (40,), 1000, 4096),
