@@ -23,7 +23,7 @@ import pytest
 import bit_weight_gemm_amd as bw
 import oracle
 import workloads as wl
-from gpu_util import MFMA_REL, assert_within, note, run_tq2, torch_cuda
+from gpu_util import MFMA_REL, assert_within, check_tq2_sampled, note, run_tq2, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -73,5 +73,23 @@ def test_rows_are_independent(torch):
         # a single row gives the same bits as that row inside the 8-row call
         y1 = run_tq2(w, x[3:4].copy(), "mfma")
         assert np.array_equal(y1.view(np.uint32), y[3:4].view(np.uint32))
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("n", [14336, 6000])
+def test_every_m_up_to_32_sampled(torch, n):
+    """Every row count the skinny kernel takes, M = 1..32, at K = 4096: at the MLP's
+    N = 14336 (four columns per lane) and at N = 6000 (two columns per lane), so each
+    steps-in-flight, pieces-per-step and row-block configuration and the unrolled
+    passes run once; sampled outputs against the oracle."""
+    k = 4096
+    aos = wl.mlp_inputs(1)[0] if n == 14336 else wl.sweep_weight(n, k)
+    x32 = wl.random_x(32, k, 7)
+    w = bw.tq2_upload(aos, n, k)
+    try:
+        for m in range(1, 33):
+            check_tq2_sampled(aos, n, k, np.ascontiguousarray(x32[:m]), "mfma", f"every M: M={m} N={n}", count=1024,
+                              w=w)
     finally:
         w.close()
